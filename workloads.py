@@ -1,0 +1,130 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module holds no attention arithmetic: it only defines the workload
+shapes and draws Q, K, V and key lengths from a seed. Both the HIP path's
+tests / benchmark and the float64 oracle are fed from here, which is the one
+thing the two sides share.
+
+The pages measure on an organiser harness that draws synthetic tensors from a
+fixed seed (devpost "gpu-transformer-optimization", "Development
+environment"); that harness and its shape list are not available, so these
+five workloads, with their stated shapes and distributions, stand in for it.
+
+Recipe (every workload): a torch CPU generator seeded with `seed` draws q, k,
+v in that order as float32 N(0, 1) tensors of shape [B, H, S, d_h], each then
+cast to the workload dtype with round-to-nearest-even; where the key lengths
+are random they are drawn next, uniform on [lo, hi] inclusive. The long
+workload (3.3e9 elements per tensor) is drawn by the device generator instead,
+in the same order, and never exists on the host.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "sample_rows"]
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    S: int
+    D: int
+    dtype: torch.dtype
+    causal: bool
+    # key lengths: None -> all S keys valid (NULL key_len pointer);
+    # ("fixed", L) -> every batch has L valid keys;
+    # ("uniform", lo, hi) -> per batch uniform on [lo, hi] inclusive.
+    key_len: Optional[tuple]
+    note: str = ""
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+    @property
+    def elems(self) -> int:
+        return self.B * self.H * self.S * self.D
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 2, 64, 32, torch.float32, False, None,
+                     "oracle-sized case: fp32, non-causal, all 64 keys valid"),
+    "launch": Workload("launch", 1, 8, 128, 16, torch.float16, True, ("fixed", 128),
+                       "launch-bound: B=1, d_model=128 in 8 heads of 16"),
+    "bandwidth": Workload("bandwidth", 10000, 8, 128, 16, torch.float16, True, ("uniform", 64, 128),
+                          "HBM-bound: 80000 short heads, right-padded key lengths"),
+    "compute": Workload("compute", 16, 4, 1024, 256, torch.float16, False, ("fixed", 1024),
+                        "MFMA-bound: d_model=1024 in 4 heads of 256"),
+    "long": Workload("long", 32, 16, 100000, 64, torch.float16, True, ("fixed", 100000),
+                     "long sequence: d_model=1024 in 16 heads of 64, S=100000"),
+}
+
+
+def _draw_key_len(w: Workload, gen: torch.Generator, device) -> Optional[torch.Tensor]:
+    if w.key_len is None:
+        return None
+    kind = w.key_len[0]
+    if kind == "fixed":
+        return torch.full((w.B,), int(w.key_len[1]), dtype=torch.int32, device=device)
+    if kind == "uniform":
+        lo, hi = int(w.key_len[1]), int(w.key_len[2])
+        return torch.randint(lo, hi + 1, (w.B,), generator=gen, dtype=torch.int32,
+                             device=gen.device).to(device)
+    raise ValueError(f"unknown key_len spec {w.key_len!r}")
+
+
+def make_inputs(w: Workload, seed: int, device="cpu", gen_device: Optional[str] = None
+                ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
+    """Draw (q, k, v, key_len) for workload `w` from `seed`.
+
+    gen_device: where the generator lives ("cpu" by default; the long workload
+    uses the device generator, which must be "cuda"). Tensors are returned on
+    `device`.
+    """
+    if gen_device is None:
+        gen_device = "cuda" if w.name == "long" else "cpu"
+    gen = torch.Generator(device=gen_device)
+    gen.manual_seed(int(seed))
+    shape = (w.B, w.H, w.S, w.D)
+    out = []
+    for _ in range(3):
+        t = torch.randn(shape, generator=gen, dtype=torch.float32, device=gen_device)
+        t = t.to(w.dtype)
+        out.append(t.to(device))
+        del t
+    kl = _draw_key_len(w, gen, device)
+    return out[0], out[1], out[2], kl
+
+
+def sample_rows(B: int, H: int, S: int, n_rows: int, seed: int, tile: int = 128,
+                n_heads: Optional[int] = None) -> np.ndarray:
+    """Seeded (b, h, i) query-row sample for checking a long sequence row by row.
+
+    The sample spans `n_heads` heads (default: one per batch, head drawn at
+    random) and, in each, forced rows at the sequence ends and at tile edges
+    plus uniform draws. Returns int64 [n, 3].
+    """
+    rng = np.random.Generator(np.random.PCG64(int(seed)))
+    if n_heads is None:
+        n_heads = B
+    bs = np.arange(n_heads) % B
+    hs = rng.integers(0, H, size=n_heads)
+    per = max(1, n_rows // n_heads)
+    forced = [0, 1, 2, tile - 1, tile, tile + 1, S // 2, S - tile - 1, S - tile,
+              (S // tile) * tile - 1, (S // tile) * tile, S - 2, S - 1]
+    forced = sorted({f for f in forced if 0 <= f < S})
+    rows = []
+    for n in range(n_heads):
+        fr = forced if n % 4 == 0 else forced[:3] + forced[-3:]
+        k = max(0, per - len(fr))
+        rnd = rng.integers(0, S, size=k)
+        for i in list(fr) + list(rnd):
+            rows.append((bs[n], hs[n], i))
+    rows = np.asarray(rows, dtype=np.int64)
+    return rows[:max(n_rows, 1)] if rows.shape[0] > n_rows else rows

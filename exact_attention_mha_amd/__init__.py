@@ -1,0 +1,156 @@
+"""Exact multi-head attention forward for MI355X (gfx950).
+
+A thin ctypes binding over the C ABI in include/mha.h (libmha_gfx950.so).
+PyTorch supplies device memory and the stream; every step of the attention
+itself runs in the library's HIP kernels. There is no fallback: if the
+library is not built, or the tensors are not on a GPU, calls raise.
+
+    out, lse = forward(q, k, v, causal=True, key_len=lengths)
+
+q, k, v: contiguous [B, H, S, d_h] tensors on the GPU (float32, float16 or
+bfloat16), d_h in {16, 32, 64, 128, 256}; key_len: None or an int32 GPU
+tensor [B] of right-padded key lengths.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "forward", "load", "library_path", "library_built", "select_variant",
+    "VARIANTS", "DTYPES", "MhaError",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libmha_gfx950.so"
+
+# enum mha_variant (include/mha.h)
+VARIANTS = {"auto": 0, "f32": 1, "mfma": 2, "mfma_small": 3, "valu_d16": 4, "short": 5}
+_VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
+# enum mha_dtype
+DTYPES = {"float32": 0, "float16": 1, "bfloat16": 2}
+
+_lib = None
+
+
+class MhaError(RuntimeError):
+    """A non-zero status returned by the C ABI."""
+
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, _LIB_NAME)
+
+
+def library_built() -> bool:
+    return os.path.exists(library_path())
+
+
+def load() -> ctypes.CDLL:
+    """Load the HIP library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; build it with `python -m exact_attention_mha_amd.build` "
+            "(or __graft_entry__.build()). There is no CPU fallback.")
+    lib = ctypes.CDLL(path)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    args = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, vp, ctypes.c_int, vp]
+    lib.mha_forward.argtypes = args
+    lib.mha_forward.restype = ctypes.c_int
+    lib.mha_forward_variant.argtypes = args + [ctypes.c_int]
+    lib.mha_forward_variant.restype = ctypes.c_int
+    lib.mha_select_variant.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    lib.mha_select_variant.restype = ctypes.c_int
+    lib.mha_variant_name.argtypes = [ctypes.c_int]
+    lib.mha_variant_name.restype = ctypes.c_char_p
+    lib.mha_status_string.argtypes = [ctypes.c_int]
+    lib.mha_status_string.restype = ctypes.c_char_p
+    lib.mha_version.argtypes = []
+    lib.mha_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _dtype_code(t) -> int:
+    name = str(t.dtype).replace("torch.", "")
+    if name not in DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}; expected float32, float16 or bfloat16")
+    return DTYPES[name]
+
+
+def select_variant(B: int, H: int, S: int, d_h: int, causal: bool, dtype) -> str:
+    """Name of the kernel variant mha_forward picks for these arguments."""
+    lib = load()
+    code = DTYPES[str(dtype).replace("torch.", "")] if not isinstance(dtype, int) else dtype
+    v = lib.mha_select_variant(B, H, S, d_h, int(bool(causal)), code)
+    if v < 0:
+        raise MhaError("mha_select_variant", -v, lib.mha_status_string(-v).decode())
+    return _VARIANT_NAMES.get(v, "unknown")
+
+
+def forward(q, k, v, causal: bool = False, key_len=None, out=None, lse=None,
+            return_lse: bool = True, variant: str = "auto", stream=None
+            ) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
+    """softmax(Q K^T / sqrt(d_h) + mask) V on the GPU, plus per-row log-sum-exp.
+
+    Args:
+      q, k, v: contiguous [B, H, S, d_h] GPU tensors of one dtype.
+      causal: key j visible to query i only if j <= i.
+      key_len: None (all S keys valid) or an int32 GPU tensor [B].
+      out: optional preallocated output (same shape/dtype as q).
+      lse: optional preallocated float32 [B, H, S]; ignored if return_lse is
+        False and lse is None (then no lse is written).
+      variant: kernel variant name (see VARIANTS); "auto" picks by regime.
+      stream: a torch.cuda.Stream (default: the current stream).
+    Returns:
+      (out, lse) -- lse is None when return_lse is False and none was given.
+    """
+    import torch
+
+    lib = load()
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError(f"q, k, v must share a [B,H,S,d_h] shape, got {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, H, S, D = q.shape
+    dcode = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous GPU tensor shaped and typed like q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, H, S) or lse.dtype != torch.float32
+                            or not lse.is_contiguous() or not lse.is_cuda):
+        raise ValueError("lse must be a contiguous float32 GPU tensor [B, H, S]")
+    kl_ptr = None
+    if key_len is not None:
+        if (key_len.dtype != torch.int32 or key_len.shape != (B,) or not key_len.is_cuda
+                or not key_len.is_contiguous()):
+            raise ValueError("key_len must be a contiguous int32 GPU tensor [B]")
+        kl_ptr = key_len.data_ptr()
+    if variant not in VARIANTS:
+        raise ValueError(f"unknown variant {variant!r}; one of {sorted(VARIANTS)}")
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    status = lib.mha_forward_variant(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None,
+        B, H, S, D, int(bool(causal)), kl_ptr, dcode, st.cuda_stream, VARIANTS[variant])
+    if status != 0:
+        raise MhaError("mha_forward", status, lib.mha_status_string(status).decode())
+    return out, lse

@@ -1,0 +1,100 @@
+// Device-side helpers shared by the gfx950 attention kernels.
+//
+// Matrix-core conventions used throughout (64-lane wavefront, lane = 16*g + c,
+// c = lane & 15, g = lane >> 4):
+//   * a 16x16 fp32 MFMA result tile holds element (row 4g+i, col c) in
+//     register i of lane (g, c);
+//   * the A operand of a 16x16xK MFMA holds row c, and the B operand column c,
+//     with the K index spread over (g, element); only the correspondence
+//     between A and B matters, and every kernel fills both from the same
+//     (g, element) -> k map.
+// Scores are computed transposed, S^T = K Q^T (rows = keys, cols = queries),
+// so every lane owns one query column: row max / sum reduce inside the lane
+// and across the four lane groups only, and the probability tile P^T is
+// already laid out as the B operand of O^T += V^T P^T.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mha {
+
+typedef _Float16 f16_t;
+typedef __bf16 bf16_t;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.693147180559945309417f;
+constexpr float kLog2e = 1.442695040888963407360f;
+
+template <typename T> struct Vec;
+template <> struct Vec<f16_t> { typedef f16x8 x8; typedef f16x4 x4; };
+template <> struct Vec<bf16_t> { typedef bf16x8 x8; typedef bf16x4 x4; };
+
+// ---- matrix-core products (fp32 accumulate) ---------------------------------
+__device__ __forceinline__ f32x4 mfma_k32(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_k32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_k16(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_k16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                   __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---- transcendental helpers (single hardware instructions) ----------------
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// ---- cross-group reductions: lanes c, c+16, c+32, c+48 share a query ------
+__device__ __forceinline__ float group_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float group_sum(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// ---- conversions -------------------------------------------------------------
+template <typename T> __device__ __forceinline__ T to_t(float x);
+template <> __device__ __forceinline__ f16_t to_t<f16_t>(float x) { return (f16_t)x; }
+template <> __device__ __forceinline__ bf16_t to_t<bf16_t>(float x) { return (bf16_t)x; }
+
+template <typename T> __device__ __forceinline__ float to_f(T x) { return (float)x; }
+
+template <typename V> __device__ __forceinline__ V zero_vec() {
+  V z;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(V) / sizeof(z[0])); ++i) z[i] = 0;
+  return z;
+}
+
+// Workgroup id -> logical tile id. Consecutive workgroup ids are dispatched
+// round-robin over the 8 XCDs; this remap gives each XCD a contiguous range
+// of logical tiles, so the query tiles of one head share that XCD's L2.
+__device__ __forceinline__ uint32_t xcd_logical_id(uint32_t id, uint32_t n) {
+  const uint32_t per = n >> 3, rem = n & 7u, x = id & 7u, j = id >> 3;
+  return x * per + (x < rem ? x : rem) + j;
+}
+
+__device__ __forceinline__ int clamp_len(const int32_t* key_len, int b, int S) {
+  if (!key_len) return S;
+  int L = key_len[b];
+  return L < 0 ? 0 : (L > S ? S : L);
+}
+
+}  // namespace mha

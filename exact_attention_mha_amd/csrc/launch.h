@@ -1,0 +1,32 @@
+// Host-side launch interface between the C ABI (mha_api.cpp) and the kernel
+// translation units. Each launcher validates nothing: the ABI layer has
+// already checked pointers, sizes and alignment; a launcher returns
+// hipErrorInvalidValue only when its kernel has no instantiation for the
+// requested (dtype, d_h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mha {
+
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;              // nullable
+  const int32_t* key_len;  // nullable
+  int B, H, S, D;
+  int causal;
+  int dtype;               // enum mha_dtype
+  float c_log2;            // log2(e) / sqrt(d_h)
+};
+
+hipError_t launch_mfma(const AttnParams& p, hipStream_t s);        // general tiled
+hipError_t launch_mfma_small(const AttnParams& p, hipStream_t s);  // few rows per WG
+hipError_t launch_f32(const AttnParams& p, hipStream_t s);         // fp32 inputs
+hipError_t launch_valu_d16(const AttnParams& p, hipStream_t s);    // d_h = 16 VALU
+hipError_t launch_short(const AttnParams& p, hipStream_t s);       // S <= 128 one pass
+
+}  // namespace mha

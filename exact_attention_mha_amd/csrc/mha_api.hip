@@ -1,0 +1,140 @@
+// C ABI of the attention library: host-side validation, kernel choice and
+// launch on the caller's stream. Declarations and the contract are in
+// include/mha.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/mha.h"
+#include "launch.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool supported_d(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
+
+// Static kernel choice by regime (dtype, d_h, sequence length, head count):
+//  * fp32 inputs                         -> fp32 matrix-core kernel
+//  * S <= 128 and d_h <= 64, many heads  -> one pass per head, no rescaling
+//  * few heads (fewer than ~2 workgroups per CU with 128-row tiles)
+//                                        -> 16-row tiles, one wave each
+//  * otherwise                           -> general tiled kernel
+int choose(int64_t B, int64_t H, int64_t S, int64_t D, int dtype) {
+  if (dtype == MHA_F32) return MHA_VARIANT_F32;
+  const int64_t heads = B * H;
+  if (S <= 128 && D <= 64 && heads >= 512) return MHA_VARIANT_SHORT;
+  const int64_t wg128 = heads * ((S + 127) / 128);
+  if (wg128 < 512) return MHA_VARIANT_MFMA_SMALL;
+  return MHA_VARIANT_MFMA;
+}
+
+int validate(const void* q, const void* k, const void* v, void* out, const float* lse,
+             int64_t B, int64_t H, int64_t S, int64_t d_h, const int32_t* key_len, int dtype) {
+  if (B < 0 || H < 0 || S < 0 || d_h <= 0) return MHA_ERR_SHAPE;
+  if (dtype != MHA_F32 && dtype != MHA_F16 && dtype != MHA_BF16) return MHA_ERR_UNSUPPORTED;
+  if (!supported_d(d_h)) return MHA_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0 || S == 0) return MHA_OK;
+  if (!q || !k || !v || !out) return MHA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return MHA_ERR_MISALIGNED;
+  if ((lse && !aligned(lse, 4)) || (key_len && !aligned(key_len, 4))) return MHA_ERR_MISALIGNED;
+  if (S * d_h >= (int64_t)1 << 31) return MHA_ERR_SHAPE;  // per-head offsets are 32-bit
+  if (B * H >= (int64_t)1 << 31) return MHA_ERR_SHAPE;
+  return MHA_OK;
+}
+
+bool variant_runs(int variant, int64_t S, int64_t D, int dtype) {
+  switch (variant) {
+    case MHA_VARIANT_F32: return dtype == MHA_F32;
+    case MHA_VARIANT_MFMA:
+    case MHA_VARIANT_MFMA_SMALL: return dtype != MHA_F32;
+    case MHA_VARIANT_VALU_D16: return dtype != MHA_F32 && D == 16;
+    case MHA_VARIANT_SHORT: return dtype != MHA_F32 && S <= 128 && D <= 64;
+  }
+  return false;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mha_forward_variant(const void* q, const void* k, const void* v, void* out, float* lse,
+                        int64_t B, int64_t H, int64_t S, int64_t d_h, int causal,
+                        const int32_t* key_len, int dtype, void* stream, int variant) {
+  const int st = validate(q, k, v, out, lse, B, H, S, d_h, key_len, dtype);
+  if (st != MHA_OK) return st;
+  if (variant < 0 || variant >= MHA_VARIANT_COUNT) return MHA_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0 || S == 0) return MHA_OK;
+  if (variant == MHA_VARIANT_AUTO) variant = choose(B, H, S, d_h, dtype);
+  if (!variant_runs(variant, S, d_h, dtype)) return MHA_ERR_UNSUPPORTED;
+
+  mha::AttnParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.key_len = key_len;
+  p.B = (int)B;
+  p.H = (int)H;
+  p.S = (int)S;
+  p.D = (int)d_h;
+  p.causal = causal ? 1 : 0;
+  p.dtype = dtype;
+  p.c_log2 = (float)(1.4426950408889634074 / sqrt((double)d_h));
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipErrorInvalidValue;
+  switch (variant) {
+    case MHA_VARIANT_F32: e = mha::launch_f32(p, s); break;
+    case MHA_VARIANT_MFMA: e = mha::launch_mfma(p, s); break;
+    case MHA_VARIANT_MFMA_SMALL: e = mha::launch_mfma_small(p, s); break;
+    case MHA_VARIANT_VALU_D16: e = mha::launch_valu_d16(p, s); break;
+    case MHA_VARIANT_SHORT: e = mha::launch_short(p, s); break;
+  }
+  if (e == hipErrorInvalidConfiguration) return MHA_ERR_SHAPE;
+  return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
+}
+
+int mha_forward(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
+                int64_t H, int64_t S, int64_t d_h, int causal, const int32_t* key_len, int dtype,
+                void* stream) {
+  return mha_forward_variant(q, k, v, out, lse, B, H, S, d_h, causal, key_len, dtype, stream,
+                             MHA_VARIANT_AUTO);
+}
+
+int mha_select_variant(int64_t B, int64_t H, int64_t S, int64_t d_h, int causal, int dtype) {
+  (void)causal;
+  if (B < 0 || H < 0 || S < 0 || d_h <= 0) return -MHA_ERR_SHAPE;
+  if (dtype != MHA_F32 && dtype != MHA_F16 && dtype != MHA_BF16) return -MHA_ERR_UNSUPPORTED;
+  if (!supported_d(d_h)) return -MHA_ERR_UNSUPPORTED;
+  return choose(B, H, S, d_h, dtype);
+}
+
+const char* mha_variant_name(int variant) {
+  switch (variant) {
+    case MHA_VARIANT_AUTO: return "auto";
+    case MHA_VARIANT_F32: return "f32";
+    case MHA_VARIANT_MFMA: return "mfma";
+    case MHA_VARIANT_MFMA_SMALL: return "mfma_small";
+    case MHA_VARIANT_VALU_D16: return "valu_d16";
+    case MHA_VARIANT_SHORT: return "short";
+  }
+  return "unknown";
+}
+
+const char* mha_status_string(int status) {
+  switch (status) {
+    case MHA_OK: return "ok";
+    case MHA_ERR_NULL: return "null pointer argument";
+    case MHA_ERR_SHAPE: return "invalid or too large shape";
+    case MHA_ERR_UNSUPPORTED: return "unsupported head size, dtype or variant";
+    case MHA_ERR_MISALIGNED: return "misaligned pointer";
+    case MHA_ERR_HIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int mha_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+/*
+ * mha.h -- C ABI of the gfx950 exact multi-head attention forward library.
+ *
+ * Computes, for every batch b and head h,
+ *     out = softmax(Q K^T / sqrt(d_h) + mask) V
+ * over [B, H, S, d_h] tensors, with an optional causal mask and right-padded
+ * per-batch key lengths, plus the per-row log-sum-exp. The definition is the
+ * textbook five-op attention (devpost "gpu-transformer-optimization",
+ * section 2.1, ops (1)-(5)); the kernels evaluate it with the running-max /
+ * running-sum recurrence of the same section, so the [B, H, S, S] score
+ * tensor never reaches device memory.
+ *
+ * Mask: key j is visible to query row i iff j < L_b and, when causal,
+ * j <= i, where L_b = key_len[b] clamped to [0, S] (or S when key_len is
+ * NULL). Padded query rows (i >= L_b) still produce output: they attend to
+ * keys 0..L_b-1. A row with no visible key (L_b == 0) gets out = 0 and
+ * lse = -inf. Padded key/value rows (j >= L_b) are never read, so their
+ * contents (even NaN) cannot affect any result.
+ *
+ * Precision: fp16 / bf16 inputs are multiplied on the matrix cores with fp32
+ * accumulation; softmax arithmetic is fp32; out is rounded once to the input
+ * dtype. fp32 inputs are computed in fp32 throughout.
+ *
+ * All functions are thread-safe; the library keeps no per-call state and
+ * allocates no memory.
+ */
+#ifndef EXACT_ATTENTION_MHA_AMD_MHA_H
+#define EXACT_ATTENTION_MHA_AMD_MHA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and out. */
+enum mha_dtype {
+  MHA_F32 = 0,
+  MHA_F16 = 1,
+  MHA_BF16 = 2
+};
+
+/* Return codes. Validation errors are detected on the host before anything
+ * is enqueued; nothing is launched when a call returns an error. */
+enum mha_status {
+  MHA_OK = 0,
+  MHA_ERR_NULL = 1,        /* a required pointer is NULL */
+  MHA_ERR_SHAPE = 2,       /* negative size, or sizes beyond the 32-bit
+                              per-head / grid limits stated below */
+  MHA_ERR_UNSUPPORTED = 3, /* d_h or dtype or variant not supported */
+  MHA_ERR_MISALIGNED = 4,  /* q/k/v/out not 16-byte aligned, lse/key_len not
+                              4-byte aligned */
+  MHA_ERR_HIP = 5          /* the kernel launch itself failed */
+};
+
+/* Kernel variants. MHA_VARIANT_AUTO picks by (dtype, d_h, causal, B*H, S);
+ * the others force one kernel for A/B measurement and testing. Every variant
+ * computes the same result to within the fp32 rounding of its own
+ * accumulation order. */
+enum mha_variant {
+  MHA_VARIANT_AUTO = 0,
+  MHA_VARIANT_F32 = 1,        /* fp32 inputs: fp32 matrix-core kernel        */
+  MHA_VARIANT_MFMA = 2,       /* fp16/bf16 general tiled kernel, any d_h     */
+  MHA_VARIANT_MFMA_SMALL = 3, /* fp16/bf16, 16-32 query rows per workgroup:
+                                 more workgroups for launch-bound shapes     */
+  MHA_VARIANT_VALU_D16 = 4,   /* fp16/bf16 d_h = 16 on the vector ALUs       */
+  MHA_VARIANT_SHORT = 5,      /* fp16/bf16 d_h <= 64, S <= 128: one pass per
+                                 head, no rescaling                          */
+  MHA_VARIANT_COUNT = 6
+};
+
+/*
+ * mha_forward -- enqueue one attention forward on `stream`.
+ *
+ *   q, k, v  device pointers, contiguous [B, H, S, d_h] of `dtype`,
+ *            16-byte aligned. Read only.
+ *   out      device pointer, contiguous [B, H, S, d_h] of `dtype`, 16-byte
+ *            aligned. Written in full. Must not overlap q, k or v.
+ *   lse      device pointer to contiguous fp32 [B, H, S] or NULL (not
+ *            written). lse[b,h,i] = ln(sum over visible j of
+ *            exp(q_i . k_j / sqrt(d_h))), -inf for rows with no visible key.
+ *   B, H, S  batch, heads, sequence length (>= 0; any of them 0 is a no-op
+ *            returning MHA_OK). S * d_h must be < 2^31 and the launch must
+ *            fit a 2^31-1 workgroup grid.
+ *   d_h      head dimension: 16, 32, 64, 128 or 256.
+ *   causal   non-zero: key j visible to row i only if j <= i.
+ *   key_len  device pointer to int32[B] or NULL (all S keys valid). Values
+ *            are clamped to [0, S] on the device (the host never reads them).
+ *   dtype    enum mha_dtype.
+ *   stream   hipStream_t to enqueue on; NULL = the null stream.
+ *
+ * Ownership: the caller allocates and owns every buffer and must keep them
+ * alive until the stream has passed this call. The call is asynchronous:
+ * device-side faults surface at the caller's next synchronisation.
+ * Returns an enum mha_status code; no output is written on error.
+ */
+int mha_forward(const void* q, const void* k, const void* v, void* out, float* lse,
+                int64_t B, int64_t H, int64_t S, int64_t d_h, int causal,
+                const int32_t* key_len, int dtype, void* stream);
+
+/* mha_forward with an explicit kernel variant (enum mha_variant). Returns
+ * MHA_ERR_UNSUPPORTED when the variant cannot run this (dtype, d_h, S). */
+int mha_forward_variant(const void* q, const void* k, const void* v, void* out, float* lse,
+                        int64_t B, int64_t H, int64_t S, int64_t d_h, int causal,
+                        const int32_t* key_len, int dtype, void* stream, int variant);
+
+/* The variant mha_forward would launch for these arguments (host-only, no
+ * GPU call), or a negative mha_status code if the arguments are invalid. */
+int mha_select_variant(int64_t B, int64_t H, int64_t S, int64_t d_h, int causal, int dtype);
+
+/* Static name of a variant ("mfma", "valu_d16", ...) or "unknown". */
+const char* mha_variant_name(int variant);
+
+/* Static description of a status code. */
+const char* mha_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int mha_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_MHA_AMD_MHA_H */

@@ -96,15 +96,19 @@ def _softmax_rows(s: np.ndarray, mask: np.ndarray, v: np.ndarray):
     return out, lse
 
 
-def attention(q, k, v, causal: bool = False, key_len=None, heads_per_chunk: int = 512):
+def attention(q, k, v, causal: bool = False, key_len=None, heads_per_chunk: int = 512,
+              threads: int = 1):
     """Exact attention over [B, H, S, d_h] inputs.
 
     Args:
       q, k, v: arrays or tensors of shape [B, H, S, d_h], any float dtype.
       causal:  apply the causal mask (key j visible to query i only if j <= i).
       key_len: per-batch valid key count (length B) or None for all S valid.
-      heads_per_chunk: how many (b, h) score matrices to materialise at once;
-        only bounds memory, the arithmetic per head is unchanged.
+      heads_per_chunk: how many (b, h) score matrices to materialise at once
+        (further capped so one chunk's scores stay near 1 GB); only bounds
+        memory, the arithmetic per head is unchanged.
+      threads: independent chunks of heads evaluated concurrently (numpy
+        releases the GIL); the arithmetic per head is unchanged.
 
     Returns:
       (out, lse): float64 arrays [B, H, S, d_h] and [B, H, S].
@@ -121,20 +125,33 @@ def attention(q, k, v, causal: bool = False, key_len=None, heads_per_chunk: int 
         return out, lse
     # Batches sharing a key length share a mask; group them so one matmul call
     # covers many heads.
+    heads_per_chunk = max(1, min(heads_per_chunk, (1 << 27) // (S * S)))
     bpc = max(1, heads_per_chunk // max(H, 1))
+    jobs = []
     for L in np.unique(kl):
         bs = np.nonzero(kl == L)[0]
-        mask = valid_mask(S, int(L), causal)
         for c0 in range(0, bs.shape[0], bpc):
-            sel = bs[c0:c0 + bpc]
-            s = (q[sel] @ np.swapaxes(k[sel], -1, -2)) * scale   # (1), (2)
-            # Padded value rows (j >= L) carry zero weight; zero them so that
-            # whatever they hold (even NaN) cannot leak in through 0 * NaN.
-            vv = v[sel].copy()
-            vv[..., int(L):, :] = 0.0
-            o, l = _softmax_rows(s, mask, vv)
-            out[sel] = o
-            lse[sel] = l
+            jobs.append((int(L), bs[c0:c0 + bpc]))
+
+    def run(job):
+        L, sel = job
+        mask = valid_mask(S, L, causal)
+        s = (q[sel] @ np.swapaxes(k[sel], -1, -2)) * scale        # (1), (2)
+        # Padded value rows (j >= L) carry zero weight; zero them so that
+        # whatever they hold (even NaN) cannot leak in through 0 * NaN.
+        vv = v[sel].copy()
+        vv[..., L:, :] = 0.0
+        o, l = _softmax_rows(s, mask, vv)
+        out[sel] = o
+        lse[sel] = l
+
+    if threads > 1 and len(jobs) > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(run, jobs))
+    else:
+        for job in jobs:
+            run(job)
     return out, lse
 
 

@@ -1,0 +1,97 @@
+"""Host-side checks of the C ABI: the library loads on a machine without a GPU,
+exports every function include/mha.h declares, and rejects invalid arguments
+on the host before anything is enqueued (no kernel runs in these tests)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mha.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(mha_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for want in ("mha_forward", "mha_forward_variant", "mha_select_variant",
+                 "mha_status_string", "mha_variant_name", "mha_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(mha):
+    lib = ctypes.CDLL(mha.library_path())
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_status_and_variant_strings(mha):
+    lib = mha.load()
+    assert lib.mha_status_string(0) == b"ok"
+    for code in range(1, 6):
+        assert lib.mha_status_string(code) not in (b"ok", b"unknown status")
+    assert lib.mha_status_string(99) == b"unknown status"
+    for name, code in mha.VARIANTS.items():
+        assert lib.mha_variant_name(code).decode() == name
+    assert lib.mha_version() >= 100
+
+
+def _fwd(lib, q=0x1000, k=0x2000, v=0x3000, out=0x4000, lse=None, B=1, H=1, S=16, D=64,
+         causal=0, key_len=None, dtype=1, variant=0):
+    return lib.mha_forward_variant(q, k, v, out, lse, B, H, S, D, causal, key_len, dtype, None, variant)
+
+
+def test_validation_codes(mha):
+    lib = mha.load()
+    assert _fwd(lib, q=None) == 1                 # MHA_ERR_NULL
+    assert _fwd(lib, out=None) == 1
+    assert _fwd(lib, B=-1) == 2                   # MHA_ERR_SHAPE
+    assert _fwd(lib, S=-5) == 2
+    assert _fwd(lib, D=0) == 2
+    assert _fwd(lib, D=48) == 3                   # MHA_ERR_UNSUPPORTED head size
+    assert _fwd(lib, D=8) == 3
+    assert _fwd(lib, dtype=7) == 3
+    assert _fwd(lib, variant=99) == 3
+    assert _fwd(lib, variant=4, D=64) == 3        # VALU kernel is d_h = 16 only
+    assert _fwd(lib, variant=1, dtype=1) == 3     # fp32 kernel needs fp32 inputs
+    assert _fwd(lib, variant=2, dtype=0) == 3
+    assert _fwd(lib, variant=5, S=129) == 3       # short kernel is S <= 128
+    assert _fwd(lib, variant=5, D=128) == 3
+    assert _fwd(lib, q=0x1008) == 4               # MHA_ERR_MISALIGNED
+    assert _fwd(lib, lse=0x5002) == 4
+    assert _fwd(lib, key_len=0x6001) == 4
+    assert _fwd(lib, S=1 << 26, D=64) == 2        # S * d_h >= 2^31
+    assert _fwd(lib, B=1 << 16, H=1 << 15) == 2   # B * H >= 2^31
+
+
+def test_empty_problems_are_noops(mha):
+    lib = mha.load()
+    # zero-size calls return OK without touching the (bogus) pointers
+    assert _fwd(lib, B=0) == 0
+    assert _fwd(lib, H=0, q=None) == 0
+    assert _fwd(lib, S=0) == 0
+
+
+def test_variant_selection(mha):
+    import torch
+    sel = mha.select_variant
+    assert sel(1, 2, 64, 32, False, torch.float32) == "f32"
+    assert sel(1, 8, 128, 16, True, torch.float16) == "mfma_small"
+    assert sel(10000, 8, 128, 16, True, torch.float16) == "short"
+    assert sel(16, 4, 1024, 256, False, torch.float16) == "mfma"
+    assert sel(32, 16, 100000, 64, True, torch.float16) == "mfma"
+    with pytest.raises(mha.MhaError):
+        sel(1, 1, 16, 48, False, torch.float16)
+
+
+def test_python_binding_rejects_cpu_tensors(mha):
+    import torch
+    x = torch.zeros(1, 1, 16, 16, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        mha.forward(x, x, x)

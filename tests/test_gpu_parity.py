@@ -1,0 +1,182 @@
+"""GPU parity: the HIP path (through the C ABI binding) against the float64
+oracle, element by element, under the accuracy rule |u-r| <= 2e-3 or
+|u-r| <= 2e-2 |r| (devpost "optimized-gpu-kernels-for-transformer-layers",
+Inspiration). Worst-element error grows with the number of elements checked
+(devpost "transformerkernel ... Tesla T4", Challenges), so every workload is
+run over many seeds."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import check_full, check_rows, run_gpu, workload_case, THREADS
+from workloads import WORKLOADS, make_inputs, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _report(label, fracs):
+    fo = max(f[0] for f in fracs)
+    fl = max(f[1] for f in fracs)
+    print(f"{label}: worst out budget {fo:.3f}, worst lse budget {fl:.4f}", flush=True)
+
+
+# ---------------------------------------------------------------- workloads
+
+@pytest.mark.parametrize("chunk", range(4))
+def test_tiny_200_seeds(mha, chunk):
+    w = WORKLOADS["tiny"]
+    _report(f"tiny chunk {chunk}", [workload_case(mha, w, s) for s in range(50 * chunk, 50 * chunk + 50)])
+
+
+@pytest.mark.parametrize("chunk", range(4))
+def test_launch_200_seeds(mha, chunk):
+    w = WORKLOADS["launch"]
+    _report(f"launch chunk {chunk}", [workload_case(mha, w, s) for s in range(50 * chunk, 50 * chunk + 50)])
+
+
+@pytest.mark.parametrize("variant", ["mfma", "mfma_small", "short", "valu_d16"])
+def test_launch_every_variant(mha, variant):
+    w = WORKLOADS["launch"]
+    _report(f"launch {variant}", [workload_case(mha, w, s, variant) for s in range(20)])
+
+
+@pytest.mark.parametrize("variant", ["auto", "mfma", "mfma_small", "short", "valu_d16"])
+def test_bandwidth_shape_reduced_batch(mha, variant):
+    """The bandwidth workload's per-head shape (S=128, d_h=16, causal, key
+    lengths uniform on [64, 128]) at B=64, every element checked."""
+    w = WORKLOADS["bandwidth"].with_(B=64)
+    _report(f"bandwidth B=64 {variant}", [workload_case(mha, w, s, variant) for s in range(10)])
+
+
+@pytest.mark.parametrize("chunk", range(5))
+def test_bandwidth_full_size_sampled(mha, chunk):
+    """Full B=10000 launch as timed by the benchmark; 4096 sampled rows per
+    seed against exact oracle rows, plus output-wide properties."""
+    w = WORKLOADS["bandwidth"]
+    fr = []
+    for seed in range(5 * chunk, 5 * chunk + 5):
+        q, k, v, kl = make_inputs(w, seed)
+        out, lse = run_gpu(mha, q, k, v, kl, w.causal)
+        assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+        rows = sample_rows(w.B, w.H, w.S, 4096, seed=seed, tile=16, n_heads=512)
+        fr.append(check_rows(out, lse, q, k, v, kl, w.causal, rows, f"bandwidth seed {seed}"))
+        # row 0 of every head sees key 0 only: out = v_0 (up to one rounding)
+        torch.testing.assert_close(out[:, :, 0].float(), v[:, :, 0].float(), rtol=0, atol=0)
+    _report(f"bandwidth full size chunk {chunk}", fr)
+
+
+def test_bandwidth_full_size_every_element(mha):
+    w = WORKLOADS["bandwidth"]
+    q, k, v, kl = make_inputs(w, 0)
+    out, lse = run_gpu(mha, q, k, v, kl, w.causal)
+    _report("bandwidth full size seed 0 (all elements)", [check_full(out, lse, q, k, v, kl, True, "bw")])
+
+
+@pytest.mark.parametrize("chunk", range(5))
+def test_compute_25_seeds(mha, chunk):
+    w = WORKLOADS["compute"]
+    _report(f"compute chunk {chunk}", [workload_case(mha, w, s) for s in range(5 * chunk, 5 * chunk + 5)])
+
+
+# ---------------------------------------------------------------- edge cases
+
+_DT = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def _variants_for(dt, D, S):
+    if dt == "f32":
+        return ["auto", "f32"]
+    v = ["auto", "mfma", "mfma_small"]
+    if S <= 128 and D <= 64:
+        v.append("short")
+    if D == 16:
+        v.append("valu_d16")
+    return v
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("D", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("S", [1, 17, 65, 128, 200])
+@pytest.mark.parametrize("causal", [False, True])
+def test_edge_shapes(mha, dt, D, S, causal):
+    """Ragged and tiny sequences, every head size and dtype, key lengths
+    {S, 0, 1, S//2 + 1} (0 = a batch with no visible key), every variant that
+    accepts the shape."""
+    from workloads import Workload
+    B = 4
+    w = Workload("edge", B, 3, S, D, _DT[dt], causal, None)
+    q, k, v, _ = make_inputs(w, seed=S * 7 + D)
+    kl = torch.tensor([S, 0, 1, S // 2 + 1], dtype=torch.int32)
+    for variant in _variants_for(dt, D, S):
+        out, lse = run_gpu(mha, q, k, v, kl, causal, variant)
+        check_full(out, lse, q, k, v, kl, causal, f"{dt} D={D} S={S} causal={causal} {variant}")
+        assert (out[1] == 0).all() and (lse[1] == -math.inf).all()
+
+
+@pytest.mark.parametrize("variant", ["auto", "mfma", "mfma_small", "short", "valu_d16"])
+def test_padded_keys_never_read(mha, variant):
+    """NaN / Inf in padded K and V rows must not reach any output."""
+    w = WORKLOADS["bandwidth"].with_(B=32)
+    q, k, v, kl = make_inputs(w, 3)
+    for b in range(w.B):
+        k[b, :, int(kl[b]):] = float("nan")
+        v[b, :, int(kl[b]):] = float("inf")
+    out, lse = run_gpu(mha, q, k, v, kl, True, variant)
+    assert torch.isfinite(out).all()
+    check_full(out, lse, q, k, v, kl, True, f"poisoned padding {variant}")
+
+
+@pytest.mark.parametrize("scale", [1e-3, 10.0, 30.0])
+@pytest.mark.parametrize("D,S", [(64, 300), (256, 130), (16, 128)])
+def test_adversarial_input_scales(mha, scale, D, S):
+    from workloads import Workload
+    w = Workload("adv", 2, 2, S, D, torch.float16, True, None)
+    q, k, v, _ = make_inputs(w, 11)
+    q = (q.float() * scale).half()
+    k = (k.float() * scale).half()
+    out, lse = run_gpu(mha, q, k, v, None, True)
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    check_full(out, lse, q, k, v, None, True, f"scale {scale} D={D}")
+
+
+def test_deterministic(mha):
+    w = WORKLOADS["compute"].with_(B=2)
+    q, k, v, kl = make_inputs(w, 5)
+    a = run_gpu(mha, q, k, v, kl, w.causal)
+    b = run_gpu(mha, q, k, v, kl, w.causal)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_outputs_stay_inside_their_buffers(mha):
+    """Guard bands before and after out / lse are never written."""
+    B, H, S, D = 2, 3, 77, 64
+    g = torch.Generator().manual_seed(0)
+    q, k, v = (torch.randn(B, H, S, D, generator=g).half().cuda() for _ in range(3))
+    n, nl = B * H * S * D, B * H * S
+    pad = 4096
+    buf = torch.full((pad + n + pad,), 7.0, dtype=torch.float16, device="cuda")
+    lbuf = torch.full((pad + nl + pad,), 7.0, dtype=torch.float32, device="cuda")
+    out = buf[pad:pad + n].view(B, H, S, D)
+    lse = lbuf[pad:pad + nl].view(B, H, S)
+    mha.forward(q, k, v, causal=True, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert (buf[:pad] == 7).all() and (buf[pad + n:] == 7).all()
+    assert (lbuf[:pad] == 7).all() and (lbuf[pad + nl:] == 7).all()
+    check_full(out.cpu(), lse.cpu(), q.cpu(), k.cpu(), v.cpu(), None, True, "guard bands")
+
+
+def test_without_lse_and_on_a_side_stream(mha):
+    B, H, S, D = 1, 2, 300, 64
+    g = torch.Generator().manual_seed(1)
+    q, k, v = (torch.randn(B, H, S, D, generator=g).half().cuda() for _ in range(3))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out, lse = mha.forward(q, k, v, causal=False, return_lse=False, stream=s)
+    s.synchronize()
+    assert lse is None
+    ro, _ = oracle.attention(q.cpu(), k.cpu(), v.cpu())
+    assert oracle.gate(out.cpu(), ro).all()

@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Attention forward benchmark on one MI355X.
+
+    python bench.py [--workload launch|bandwidth|compute|long|tiny]
+                    [--steps K] [--warmup W] [--gpus 1]
+
+One step is one exact attention forward (one launch of the library's kernel)
+over a batch of seeded synthetic inputs already resident in device memory.
+Prints ONE JSON line: throughput in TFLOP/s counted on the visible (query,
+key) pairs only (4 * d_h flops per pair: two matrix products), the roofline
+of the kernel (achieved vs MI355X peak, from per-launch HIP events on the
+stream the kernel runs on), and the float64 CPU oracle timed on a bounded
+sample of the same workload on this host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, GB/s
+PEAK_MFMA_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}  # dense matrix-core peaks
+MALL_BYTES = 256 << 20           # working sets below this are rotated over buffer sets
+
+DEFAULT_STEPS = {"tiny": 2000, "launch": 2000, "bandwidth": 100, "compute": 200, "long": 4}
+DEFAULT_WARMUP = {"tiny": 50, "launch": 50, "bandwidth": 5, "compute": 10, "long": 1}
+BOUND = {"tiny": "hbm", "launch": "hbm", "bandwidth": "hbm", "compute": "mfma", "long": "mfma"}
+KERNEL_SOURCES = ("attn_common.h", "attn_mfma.hip", "attn_short.hip", "attn_f32.hip",
+                  "attn_valu.hip", "mha_api.hip")
+
+
+def dtype_tag(dt) -> str:
+    return {"torch.float16": "f16", "torch.bfloat16": "bf16", "torch.float32": "f32"}[str(dt)]
+
+
+def pair_count(w, kl_cpu) -> int:
+    """Visible (query, key) pairs over all heads, from the drawn key lengths."""
+    S = w.S
+    Ls = [S] * w.B if kl_cpu is None else [max(0, min(S, int(x))) for x in kl_cpu.tolist()]
+    tot = 0
+    for L in Ls:
+        tot += (L * (L + 1) // 2 + (S - L) * L) if w.causal else S * L
+    return tot * w.H
+
+
+def algorithmic_bytes(w, kl_cpu, esize: int) -> int:
+    S, D = w.S, w.D
+    Ls = [S] * w.B if kl_cpu is None else [max(0, min(S, int(x))) for x in kl_cpu.tolist()]
+    qo = 2 * w.B * w.H * S * D * esize
+    kv = 2 * w.H * D * esize * sum(Ls)
+    lse = 4 * w.B * w.H * S
+    kl = 0 if kl_cpu is None else 4 * w.B
+    return qo + kv + lse + kl
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_attention_mha_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, per_launch_src_hash: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != per_launch_src_hash:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, kl, flops_per_pair_unit: int, budget_s: float = 12.0):
+    """Time the float64 oracle as it stands on a bounded sample of this workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    avail = len(os.sched_getaffinity(0))
+    threads = max(1, min(16, avail))
+    # the long workload stays on the device: the oracle copies back only the
+    # heads its sampled rows need
+    qc, kc, vc = (q, k, v) if w.name == "long" else (q.cpu(), k.cpu(), v.cpu())
+    klc = None if kl is None else kl.cpu()
+    D = w.D
+    if w.name == "long":
+        from workloads import sample_rows
+        rows = sample_rows(w.B, w.H, w.S, 256, seed=0, tile=128, n_heads=4)
+        pairs = int(sum(min(int(i) + 1, w.S) for i in rows[:, 2]))
+        t0 = time.perf_counter()
+        oracle.attention_rows(qc, kc, vc, rows, causal=True, key_len=klc)
+        dt = time.perf_counter() - t0
+        sample = f"{rows.shape[0]} query rows of S=100000 in 4 heads (exact rows)"
+        reps = 1
+    else:
+        if w.name == "bandwidth":
+            nb = 2000
+            qc, kc, vc, klc = qc[:nb], kc[:nb], vc[:nb], klc[:nb]
+            sample = f"first {nb} of {w.B} batches"
+            ws = w.with_(B=nb)
+        else:
+            ws = w
+            sample = "whole workload, repeated"
+        pairs = pair_count(ws, klc)
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.attention(qc, kc, vc, causal=w.causal, key_len=klc, threads=threads)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt > budget_s or (w.name == "bandwidth" and reps >= 1):
+                break
+        if reps > 1:
+            sample += f" x{reps}"
+    tflops = flops_per_pair_unit * pairs * reps / dt / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": max(blas, threads if w.name != "long" else blas),
+            "kind": "oracle", "sample": sample, "seconds": round(dt, 3),
+            "host_cores_available": avail}
+
+
+def copy_calibration(nbytes: int, reps: int):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    src = torch.empty(nbytes // 2, dtype=torch.float16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": nbytes, "bytes_written": nbytes, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="launch",
+                    choices=["tiny", "launch", "bandwidth", "compute", "long"])
+    ap.add_argument("--variant", default="auto")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration << 20, 10)
+        return
+
+    import exact_attention_mha_amd as mha
+    from workloads import WORKLOADS, make_inputs
+
+    mha.load()  # raises if the HIP library is missing: there is no fallback
+    w = WORKLOADS[args.workload]
+    K = args.steps if args.steps is not None else DEFAULT_STEPS[w.name]
+    W = args.warmup if args.warmup is not None else DEFAULT_WARMUP[w.name]
+    dev = torch.device("cuda:0")
+    tag = dtype_tag(w.dtype)
+    esize = torch.tensor([], dtype=w.dtype).element_size()
+
+    q, k, v, kl = make_inputs(w, args.seed, device=dev)
+    kl_cpu = None if kl is None else kl.cpu()
+    pairs = pair_count(w, kl_cpu)
+    flops = 4 * w.D * pairs
+    conv_flops = 4 * w.B * w.H * w.S * w.S * w.D * (0.5 if w.causal else 1.0)
+    nbytes = algorithmic_bytes(w, kl_cpu, esize)
+
+    # rotate over several buffer sets when the working set would sit in the
+    # 256 MB MALL, so repeated launches do not read warm inputs
+    nsets = 1 if nbytes >= MALL_BYTES else max(3, min(8, math.ceil(2 * MALL_BYTES / max(nbytes, 1))))
+    sets = [(q, k, v)]
+    for _ in range(nsets - 1):
+        sets.append((q.clone(), k.clone(), v.clone()))
+    outs = [(torch.empty_like(q), torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev))
+            for _ in range(nsets)]
+    stream = torch.cuda.current_stream(dev)
+    variant_name = mha.select_variant(w.B, w.H, w.S, w.D, w.causal, w.dtype) \
+        if args.variant == "auto" else args.variant
+
+    def step(i):
+        qq, kk, vv = sets[i % nsets]
+        o, l = outs[i % nsets]
+        mha.forward(qq, kk, vv, causal=w.causal, key_len=kl, out=o, lse=l,
+                    variant=args.variant, stream=stream)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K back-to-back steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(K):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = e0.elapsed_time(e1)
+    ms_per_step = max(ev_ms, wall * 1e3) / K
+
+    # ---- kernel duration: HIP event pair around each launch on its stream
+    nk = min(K, 200)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nk)]
+    for i in range(nk):
+        evs[i][0].record(stream)
+        step(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    kms = sorted(a.elapsed_time(b) for a, b in evs)
+    k_avg_ms = sum(kms) / nk
+    k_med_ms = kms[nk // 2]
+
+    bound = BOUND[w.name]
+    if bound == "hbm":
+        achieved, peak, unit = nbytes / (k_avg_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved, peak, unit = flops / (k_avg_ms * 1e-3) / 1e12, PEAK_MFMA_TFLOPS[tag], "TFLOP/s"
+    src_hash = kernel_source_hash()
+    traffic = stored_traffic(w.name, src_hash)
+
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    res = {
+        "metric": "attention TFLOP/s (causal-adjusted) and % of MI355X MFMA/HBM roofline",
+        "value": round(value, 4),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": tag,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "B": w.B, "H": w.H, "S": w.S, "d_h": w.D, "causal": w.causal,
+            "key_len": (None if w.key_len is None else list(w.key_len)), "seed": args.seed,
+            "variant": variant_name, "buffer_sets": nsets, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 5), "traffic": traffic,
+            "kernel_avg_us": round(k_avg_ms * 1e3, 3), "kernel_median_us": round(k_med_ms * 1e3, 3),
+            "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+            "kernel_source_hash": src_hash,
+        },
+        "flops_per_step": flops,
+        "conventional_causal_adjusted_flops": conv_flops,
+        "visible_pairs": pairs,
+        "hbm_gbs_per_step": round(nbytes / (ms_per_step * 1e-3) / 1e9, 3),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, q, k, v, kl, 4 * w.D)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -53,6 +53,16 @@ __device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// ---- LDS transpose read (gfx950 ds_read_b64_tr_b16) -------------------------
+// Within each group of 16 lanes, lanes 4r..4r+3 each supply the address of 4
+// consecutive 16-bit elements; together they form row r (16 elements) of a
+// 4 x 16 tile. Lane j of the group receives column j: element j of rows
+// 0, 1, 2, 3. Used to read V^T operands from a row-major V tile.
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+}
+
 // ---- transcendental helpers (single hardware instructions) ----------------
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

@@ -2,27 +2,34 @@
 //
 // One workgroup owns one (batch, head) and a block of BQ = NW*NQT*16 query
 // rows; each wave owns NQT 16-row query tiles whose Q fragments stay in
-// registers. The workgroup walks key blocks of BK rows in order: K (row
-// major) and V (transposed, so a lane reads 8 consecutive keys of one
-// output column) are staged in LDS, then each wave computes
+// registers. The workgroup walks key blocks of BK rows in order. K and V are
+// staged row major in LDS, double buffered: the next block's global loads are
+// issued before the current block's arithmetic and written to the other LDS
+// buffer after it, so there is one barrier per block. Each wave computes
 //     S^T = K Q^T            (16x16x32 MFMA, fp32 accumulate)
-//     online softmax update  (running max m, running sum l, rescale O by
+//     online softmax update  (running max m, running sum l, O rescaled by
 //                             exp2(m_old - m_new))
-//     O^T += V^T P^T         (P rounded to the input dtype; bf16 uses a
-//                             bf16 head + bf16 remainder, two products)
+//     O^T += V^T P^T         (V^T read with the LDS transpose read; P rounded
+//                             to the input dtype, bf16 as head + remainder)
 // following the running-max recurrence of devpost
 // "gpu-transformer-optimization", section 2.1 ("The mechanism: online
-// softmax"). Key blocks past the causal diagonal or the key length are
-// skipped; only blocks that straddle either boundary are masked elementwise.
+// softmax"). The rescale is lazy: the running max only moves when a block's
+// maximum exceeds it by more than 2^8 (probabilities then stay <= 256, which
+// fp32 sums and fp16 probabilities hold without loss), so O is rarely
+// touched; numerator and denominator always share the same max, so the
+// result is the same quotient. Key blocks past the causal diagonal or the key
+// length are skipped; only blocks that straddle either boundary are masked.
 //
 // Key order inside a 32-key pair: the two 16-key S^T tiles take keys
 // 8*(r/4) + r%4 and 8*(r/4) + 4 + r%4 on their row r, so that lane group g
-// ends up holding keys 8g..8g+7 of the pair, which is exactly the K index
-// run of the P^T operand of the PV product and one 16-byte read of V^T.
+// holds keys 8g..8g+7 of the pair, which is the K index run of the P^T
+// operand and of two transpose reads of V.
 #include "attn_common.h"
 #include "launch.h"
 
 namespace mha {
+
+constexpr float kRescaleSlack = 8.0f;  // log2 units: lazy rescale threshold
 
 template <typename T, int D, int NQT, int NW, int BK>
 __global__ void __launch_bounds__(NW * 64)
@@ -31,19 +38,21 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
               int H, int S, int causal, int n_qblk, float c_log2) {
   typedef typename Vec<T>::x8 T8;
   typedef typename Vec<T>::x4 T4;
+  constexpr int NT = NW * 64;
   constexpr int BQ = NW * NQT * 16;
-  constexpr int KSTR = D + 8;   // padded LDS row strides (elements)
-  constexpr int VSTR = BK + 8;
-  constexpr int NDT = D / 16;   // output column tiles
-  constexpr int NKT = BK / 16;  // key tiles per block
-  constexpr int NKP = BK / 32;  // key pairs per block
+  constexpr int STR = D + 8;        // padded LDS row stride (elements), K and V
+  constexpr int TILE = BK * STR;    // one K or V block in LDS
+  constexpr int NDT = D / 16;       // output column tiles
+  constexpr int NKT = BK / 16;      // key tiles per block
+  constexpr int NKP = BK / 32;      // key pairs per block
   constexpr int NKC = D >= 32 ? D / 32 : 1;
-  constexpr int CPR = D / 8;    // 16-byte chunks per row
+  constexpr int CPR = D / 8;        // 16-byte chunks per row
+  constexpr int NCH = BK * CPR;     // chunks per block per tensor
+  constexpr int CPT = (NCH + NT - 1) / NT;
   constexpr bool kBf16 = __is_same(T, bf16_t);
   static_assert(BK % 32 == 0 && D % 16 == 0, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) T Ks[BK * KSTR];
-  __shared__ __attribute__((aligned(16))) T Vt[D * VSTR];
+  __shared__ __attribute__((aligned(16))) T smem[2 * 2 * TILE];  // [stage][K, V]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -69,6 +78,35 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   const bool wave_live = wq0 < S;
   const int kend_w = !wave_live ? 0 : (causal ? min(L, min(q_end, wq0 + NQT * 16)) : L);
 
+  // ---- global -> register prefetch of one K/V block, register -> LDS store
+  T8 pk[CPT], pv[CPT];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int ch = tid + j * NT;
+      const int r = ch / CPR, cc = ch - r * CPR;
+      const int key = k0 + r;
+      const bool in = (NCH % NT == 0 || ch < NCH) && key < kend;
+      pk[j] = in ? *(const T8*)(Kh + key * D + cc * 8) : zero_vec<T8>();
+      pv[j] = in ? *(const T8*)(Vh + key * D + cc * 8) : zero_vec<T8>();
+    }
+  };
+  auto lstore = [&](int st) {
+    T* Ks = smem + st * 2 * TILE;
+    T* Vs = Ks + TILE;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int ch = tid + j * NT;
+      if (NCH % NT == 0 || ch < NCH) {
+        const int r = ch / CPR, cc = ch - r * CPR;
+        *(T8*)(Ks + r * STR + cc * 8) = pk[j];
+        *(T8*)(Vs + r * STR + cc * 8) = pv[j];
+      }
+    }
+  };
+
+  if (nblk > 0) gload(0);
+
   T8 qf[NQT][NKC];
   T4 qf4[NQT];
 #pragma unroll
@@ -93,117 +131,120 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
     for (int dt = 0; dt < NDT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  if (nblk > 0) lstore(0);
+  __syncthreads();
+
   for (int kb = 0; kb < nblk; ++kb) {
     const int k0 = kb * BK;
-    if (kb) __syncthreads();  // everyone is done reading the previous block
-    // ---- stage K (row major) and V (transposed) into LDS; rows past kend
-    //      are zero-filled and never read from memory
-    for (int ch = tid; ch < BK * CPR; ch += NW * 64) {
-      const int r = ch / CPR, cc = ch - r * CPR;
-      const int key = k0 + r;
-      const T8 val = key < kend ? *(const T8*)(Kh + key * D + cc * 8) : zero_vec<T8>();
-      *(T8*)(Ks + r * KSTR + cc * 8) = val;
-    }
-    for (int ch = tid; ch < BK * CPR; ch += NW * 64) {
-      const int r = ch % BK, cc = ch / BK;
-      const int key = k0 + r;
-      const T8 val = key < kend ? *(const T8*)(Vh + key * D + cc * 8) : zero_vec<T8>();
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Vt[(cc * 8 + e) * VSTR + r] = val[e];
-    }
-    __syncthreads();
-    if (k0 >= kend_w) continue;  // wave-uniform: block is past this wave's rows
+    const bool more = kb + 1 < nblk;
+    if (more) gload(k0 + BK);  // in flight during this block's arithmetic
 
-    // ---- S^T = K Q^T for every key tile of the block
-    f32x4 s[NQT][NKT];
+    if (k0 < kend_w) {  // wave-uniform: block overlaps this wave's rows
+      const T* Ks = smem + (kb & 1) * 2 * TILE;
+      const T* Vs = Ks + TILE;
+
+      // ---- S^T = K Q^T
+      f32x4 s[NQT][NKT];
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-      const int krow = 32 * (kt >> 1) + 8 * (c >> 2) + 4 * (kt & 1) + (c & 3);
+      for (int kt = 0; kt < NKT; ++kt) {
+        const int krow = 32 * (kt >> 1) + 8 * (c >> 2) + 4 * (kt & 1) + (c & 3);
 #pragma unroll
-      for (int t = 0; t < NQT; ++t) s[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (D == 16) {
-        const T4 kf = *(const T4*)(Ks + krow * KSTR + 4 * g);
+        for (int t = 0; t < NQT; ++t) s[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (D == 16) {
+          const T4 kf = *(const T4*)(Ks + krow * STR + 4 * g);
 #pragma unroll
-        for (int t = 0; t < NQT; ++t) s[t][kt] = mfma_k16(kf, qf4[t], s[t][kt]);
-      } else {
+          for (int t = 0; t < NQT; ++t) s[t][kt] = mfma_k16(kf, qf4[t], s[t][kt]);
+        } else {
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-          const T8 kf = *(const T8*)(Ks + krow * KSTR + 32 * kc + 8 * g);
+          for (int kc = 0; kc < NKC; ++kc) {
+            const T8 kf = *(const T8*)(Ks + krow * STR + 32 * kc + 8 * g);
 #pragma unroll
-          for (int t = 0; t < NQT; ++t) s[t][kt] = mfma_k32(kf, qf[t][kc], s[t][kt]);
+            for (int t = 0; t < NQT; ++t) s[t][kt] = mfma_k32(kf, qf[t][kc], s[t][kt]);
+          }
         }
       }
-    }
 
-    // ---- mask only blocks that straddle the key length or the diagonal
-    const bool need_mask = (k0 + BK > L) || (causal && (k0 + BK - 1 > wq0));
-    if (need_mask) {
+      // ---- mask only blocks that straddle the key length or the diagonal
+      if ((k0 + BK > L) || (causal && (k0 + BK - 1 > wq0))) {
+#pragma unroll
+        for (int t = 0; t < NQT; ++t) {
+          const int row = wq0 + 16 * t + c;
+#pragma unroll
+          for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = k0 + 32 * (kt >> 1) + 8 * g + 4 * (kt & 1) + i;
+              const bool ok = key < L && (!causal || key <= row);
+              s[t][kt][i] = ok ? s[t][kt][i] : -INFINITY;
+            }
+        }
+      }
+
+      // ---- block row maxima; move the running max only when it is exceeded
+      //      by more than the slack (wave-uniform decision)
+      float mb[NQT];
+      bool grow = false;
 #pragma unroll
       for (int t = 0; t < NQT; ++t) {
-        const int row = wq0 + 16 * t + c;
+        float mx = s[t][0][0];
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = k0 + 32 * (kt >> 1) + 8 * g + 4 * (kt & 1) + i;
-            const bool ok = key < L && (!causal || key <= row);
-            if (!ok) s[t][kt][i] = -INFINITY;
-          }
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[t][kt][i]);
+        mb[t] = group_max(mx) * c_log2;  // finite: key 0 is visible to every row
+        grow |= mb[t] > m_run[t] + kRescaleSlack;
       }
-    }
-
-    // ---- online softmax update (exp2 domain, scale folded into one FMA)
-#pragma unroll
-    for (int t = 0; t < NQT; ++t) {
-      float mx = s[t][0][0];
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[t][kt][i]);
-      mx = group_max(mx);  // finite: key 0 is visible to every row once L > 0
-      const float m_new = fmaxf(m_run[t], mx * c_log2);
-      const float alpha = fast_exp2(m_run[t] - m_new);
-      m_run[t] = m_new;
-      float ls = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = fast_exp2(fmaf(s[t][kt][i], c_log2, -m_new));
-          s[t][kt][i] = pv;
-          ls += pv;
-        }
-      l_run[t] = fmaf(alpha, l_run[t], ls);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[t][dt] *= alpha;
-    }
-
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int p = 0; p < NKP; ++p) {
-      T8 pf[NQT], pl[NQT];
-#pragma unroll
-      for (int t = 0; t < NQT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float a0 = s[t][2 * p][i], a1 = s[t][2 * p + 1][i];
-          pf[t][i] = to_t<T>(a0);
-          pf[t][4 + i] = to_t<T>(a1);
-          if constexpr (kBf16) {
-            pl[t][i] = to_t<T>(a0 - to_f(pf[t][i]));
-            pl[t][4 + i] = to_t<T>(a1 - to_f(pf[t][4 + i]));
-          }
-        }
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const T8 vf = *(const T8*)(Vt + (16 * dt + c) * VSTR + 32 * p + 8 * g);
+      if (__any(grow)) {
 #pragma unroll
         for (int t = 0; t < NQT; ++t) {
-          o[t][dt] = mfma_k32(vf, pf[t], o[t][dt]);
-          if constexpr (kBf16) o[t][dt] = mfma_k32(vf, pl[t], o[t][dt]);
+          const float m_new = fmaxf(m_run[t], mb[t]);
+          const float alpha = fast_exp2(m_run[t] - m_new);
+          m_run[t] = m_new;
+          l_run[t] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) o[t][dt] *= alpha;
+        }
+      }
+
+      // ---- P = exp2(S c - m); O^T += V^T P^T, one key pair at a time
+#pragma unroll
+      for (int p = 0; p < NKP; ++p) {
+        T8 pf[NQT], pl[NQT];
+#pragma unroll
+        for (int t = 0; t < NQT; ++t) {
+          float ls = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float a0 = fast_exp2(fmaf(s[t][2 * p][i], c_log2, -m_run[t]));
+            const float a1 = fast_exp2(fmaf(s[t][2 * p + 1][i], c_log2, -m_run[t]));
+            ls += a0 + a1;
+            pf[t][i] = to_t<T>(a0);
+            pf[t][4 + i] = to_t<T>(a1);
+            if constexpr (kBf16) {
+              pl[t][i] = to_t<T>(a0 - to_f(pf[t][i]));
+              pl[t][4 + i] = to_t<T>(a1 - to_f(pf[t][4 + i]));
+            }
+          }
+          l_run[t] += ls;
+        }
+        const T* vrow = Vs + (32 * p + 8 * g + (c >> 2)) * STR + 4 * (c & 3);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const i16x4 v0 = lds_read_tr16(vrow + 16 * dt);
+          const i16x4 v1 = lds_read_tr16(vrow + 4 * STR + 16 * dt);
+          const T8 vf = __builtin_bit_cast(
+              T8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int t = 0; t < NQT; ++t) {
+            o[t][dt] = mfma_k32(vf, pf[t], o[t][dt]);
+            if constexpr (kBf16) o[t][dt] = mfma_k32(vf, pl[t], o[t][dt]);
+          }
         }
       }
     }
+
+    if (more) lstore((kb + 1) & 1);
+    __syncthreads();
   }
 
   // ---- epilogue: O / l rounded once to T; lse = ln(2) * (m + log2 l)
@@ -240,14 +281,28 @@ static hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Tile shapes (NQT query tiles per wave, NW waves, BK keys per block) per head
+// size. Entry 0 is the default; the others are kept for A/B measurement and
+// are selected with the MHA_TILE_CONFIG environment variable.
 template <typename T>
 static hipError_t launch_general(const AttnParams& p, hipStream_t s) {
+  const int cfg = p.tile_cfg;
   switch (p.D) {
     case 16: return launch_one<T, 16, 2, 4, 64>(p, s);
     case 32: return launch_one<T, 32, 2, 4, 64>(p, s);
-    case 64: return launch_one<T, 64, 2, 4, 64>(p, s);
-    case 128: return launch_one<T, 128, 2, 4, 64>(p, s);
-    case 256: return launch_one<T, 256, 2, 4, 32>(p, s);
+    case 64:
+      if (cfg == 1) return launch_one<T, 64, 4, 4, 64>(p, s);
+      if (cfg == 2) return launch_one<T, 64, 2, 4, 64>(p, s);
+      if (cfg == 3) return launch_one<T, 64, 2, 8, 128>(p, s);
+      return launch_one<T, 64, 2, 8, 64>(p, s);
+    case 128:
+      if (cfg == 1) return launch_one<T, 128, 2, 4, 64>(p, s);
+      return launch_one<T, 128, 2, 8, 64>(p, s);
+    case 256:
+      if (cfg == 1) return launch_one<T, 256, 1, 8, 32>(p, s);
+      if (cfg == 2) return launch_one<T, 256, 2, 8, 32>(p, s);
+      if (cfg == 3) return launch_one<T, 256, 1, 4, 64>(p, s);
+      return launch_one<T, 256, 2, 4, 32>(p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -21,6 +21,7 @@ struct AttnParams {
   int causal;
   int dtype;               // enum mha_dtype
   float c_log2;            // log2(e) / sqrt(d_h)
+  int tile_cfg;            // tile-shape table entry (0 = default)
 };
 
 hipError_t launch_mfma(const AttnParams& p, hipStream_t s);        // general tiled

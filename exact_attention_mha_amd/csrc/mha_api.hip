@@ -3,6 +3,7 @@
 // include/mha.h.
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "../../include/mha.h"
 #include "launch.h"
@@ -41,6 +42,16 @@ int validate(const void* q, const void* k, const void* v, void* out, const float
   if (S * d_h >= (int64_t)1 << 31) return MHA_ERR_SHAPE;  // per-head offsets are 32-bit
   if (B * H >= (int64_t)1 << 31) return MHA_ERR_SHAPE;
   return MHA_OK;
+}
+
+// Debug / A-B knob: MHA_TILE_CONFIG=<n> selects entry n of a kernel's tile
+// shape table (read once; results are identical up to fp32 summation order).
+int tile_config() {
+  static const int cfg = [] {
+    const char* e = getenv("MHA_TILE_CONFIG");
+    return e ? atoi(e) : 0;
+  }();
+  return cfg;
 }
 
 bool variant_runs(int variant, int64_t S, int64_t D, int dtype) {
@@ -82,6 +93,7 @@ int mha_forward_variant(const void* q, const void* k, const void* v, void* out, 
   p.causal = causal ? 1 : 0;
   p.dtype = dtype;
   p.c_log2 = (float)(1.4426950408889634074 / sqrt((double)d_h));
+  p.tile_cfg = tile_config();
 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipErrorInvalidValue;

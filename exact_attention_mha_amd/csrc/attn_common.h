@@ -63,6 +63,44 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
       (__attribute__((address_space(3))) i16x4*)(p));
 }
 
+// ---- buffer addressing -------------------------------------------------------
+// Raw buffer resources carry a byte range; loads past it return zero without
+// touching memory and stores past it are dropped. Kernels use this as the
+// bounds check for ragged tails (rows past S, keys past the visible range).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kBufferWord3 = 0x00020000;  // raw (untyped) buffer, gfx9 family
+constexpr int kOutOfRange = 0x7ffffff0;   // an offset past every range used here
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)nbytes, kBufferWord3);
+}
+template <typename V>
+__device__ __forceinline__ V buf_load16(rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+template <typename V>
+__device__ __forceinline__ V buf_load8(rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+template <typename V>
+__device__ __forceinline__ void buf_store8(V v, rsrc_t r, int voff) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff, 0, 0);
+}
+__device__ __forceinline__ void buf_store4(float v, rsrc_t r, int voff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, voff, 0, 0);
+}
+// Asynchronous 16-byte-per-lane copy from a buffer straight into LDS: lane i's
+// 16 bytes land at lds + 16*i (lds must be wave-uniform). Completion is
+// tracked by the vector-memory counter.
+__device__ __forceinline__ void dma16(rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, soff, 0, 0);
+}
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left unconstrained)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
 // ---- transcendental helpers (single hardware instructions) ----------------
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

@@ -2,10 +2,10 @@
 //
 // One workgroup owns one (batch, head) and a block of BQ = NW*NQT*16 query
 // rows; each wave owns NQT 16-row query tiles whose Q fragments stay in
-// registers. The workgroup walks key blocks of BK rows in order. K and V are
-// staged row major in LDS, double buffered: the next block's global loads are
-// issued before the current block's arithmetic and written to the other LDS
-// buffer after it, so there is one barrier per block. Each wave computes
+// registers. The workgroup walks key blocks of BK rows in order. K and V
+// blocks are copied from device memory straight into LDS by the buffer DMA
+// path (no staging registers), double buffered: block kb+1 is in flight while
+// block kb is consumed, with one barrier per block. Each wave computes
 //     S^T = K Q^T            (16x16x32 MFMA, fp32 accumulate)
 //     online softmax update  (running max m, running sum l, O rescaled by
 //                             exp2(m_old - m_new))
@@ -17,13 +17,25 @@
 // maximum exceeds it by more than 2^8 (probabilities then stay <= 256, which
 // fp32 sums and fp16 probabilities hold without loss), so O is rarely
 // touched; numerator and denominator always share the same max, so the
-// result is the same quotient. Key blocks past the causal diagonal or the key
+// quotient is unchanged. Key blocks past the causal diagonal or the key
 // length are skipped; only blocks that straddle either boundary are masked.
+// The row sum l can be accumulated on the matrix cores (a ones operand times
+// the same rounded P as the numerator) instead of on the vector ALUs.
 //
-// Key order inside a 32-key pair: the two 16-key S^T tiles take keys
-// 8*(r/4) + r%4 and 8*(r/4) + 4 + r%4 on their row r, so that lane group g
-// holds keys 8g..8g+7 of the pair, which is the K index run of the P^T
-// operand and of two transpose reads of V.
+// LDS layout. Rows are padded by one 16-byte slot (the DMA loads a zero
+// there), and rows are permuted inside each 32-key pair so every read is
+// bank-conflict free:
+//  * S^T tile h of pair p reads, on its A-operand row c, key
+//    8*(c/4) + 4h + c%4 of the pair (so lane group g ends up holding keys
+//    8g..8g+7 of the pair, the K index run of the P^T operand). K is stored
+//    in that read order: LDS row 16h + c holds that key, and one operand read
+//    touches 16 consecutive padded rows.
+//  * the two transpose reads of V for lane group g cover keys 8g+4s+r
+//    (s = 0, 1; r = 0..3). V key 8g+4s+r is stored at LDS row
+//    16*(g/2) + 8*(g%2) + 2r + s, so the 8 rows read together by a
+//    32-lane half of the wave are all even or all odd rows.
+// Rows past the visible key range and the pad slots come from out-of-range
+// buffer offsets, which read as zero without touching memory.
 #include "attn_common.h"
 #include "launch.h"
 
@@ -31,24 +43,34 @@ namespace mha {
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units: lazy rescale threshold
 
-template <typename T, int D, int NQT, int NW, int BK>
+// key (within a 32-key pair) stored at LDS row rho of the K / V tile
+__device__ __forceinline__ int k_key_of_row(int rho) {
+  const int h = rho >> 4, c = rho & 15;
+  return 8 * (c >> 2) + 4 * h + (c & 3);
+}
+__device__ __forceinline__ int v_key_of_row(int rho) {
+  return 16 * (rho >> 4) + 8 * ((rho >> 3) & 1) + 4 * (rho & 1) + ((rho >> 1) & 3);
+}
+
+template <typename T, int D, int NQT, int NW, int BK, bool SUM_MFMA>
 __global__ void __launch_bounds__(NW * 64)
 attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
               T* __restrict__ Op, float* __restrict__ LSEp, const int32_t* __restrict__ key_len,
               int H, int S, int causal, int n_qblk, float c_log2) {
   typedef typename Vec<T>::x8 T8;
   typedef typename Vec<T>::x4 T4;
-  constexpr int NT = NW * 64;
-  constexpr int BQ = NW * NQT * 16;
-  constexpr int STR = D + 8;        // padded LDS row stride (elements), K and V
-  constexpr int TILE = BK * STR;    // one K or V block in LDS
-  constexpr int NDT = D / 16;       // output column tiles
-  constexpr int NKT = BK / 16;      // key tiles per block
-  constexpr int NKP = BK / 32;      // key pairs per block
+  constexpr int STR = D + 8;             // padded LDS row stride (elements)
+  constexpr int SPR = D / 8 + 1;         // 16-byte slots per padded row
+  constexpr int SLOTS = BK * SPR;        // slots per K or V tile
+  constexpr int NI = (SLOTS + 63) / 64;  // DMA instructions per tile
+  constexpr int TILE = NI * 64 * 8;      // elements per tile (whole DMA instructions)
+  constexpr int NIW = (NI + NW - 1) / NW;
+  constexpr int NDT = D / 16;            // output column tiles
+  constexpr int NKT = BK / 16;           // key tiles per block
+  constexpr int NKP = BK / 32;           // key pairs per block
   constexpr int NKC = D >= 32 ? D / 32 : 1;
-  constexpr int CPR = D / 8;        // 16-byte chunks per row
-  constexpr int NCH = BK * CPR;     // chunks per block per tensor
-  constexpr int CPT = (NCH + NT - 1) / NT;
+  constexpr int RB = D * (int)sizeof(T);  // bytes per row in memory
+  constexpr int BQ = NW * NQT * 16;
   constexpr bool kBf16 = __is_same(T, bf16_t);
   static_assert(BK % 32 == 0 && D % 16 == 0, "tile shape");
 
@@ -65,10 +87,6 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   const int b = (int)(bh / (uint32_t)H);
   const int L = clamp_len(key_len, b, S);
   const int64_t head = (int64_t)bh * S * D;
-  const T* Qh = Qp + head;
-  const T* Kh = Kp + head;
-  const T* Vh = Vp + head;
-  T* Oh = Op + head;
 
   const int q_start = qb * BQ;
   const int q_end = min(S, q_start + BQ);
@@ -78,231 +96,255 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   const bool wave_live = wq0 < S;
   const int kend_w = !wave_live ? 0 : (causal ? min(L, min(q_end, wq0 + NQT * 16)) : L);
 
-  // ---- global -> register prefetch of one K/V block, register -> LDS store
-  T8 pk[CPT], pv[CPT];
-  auto gload = [&](int k0) {
+  const rsrc_t ro = make_rsrc(Op + head, (uint32_t)S * RB);
+  const rsrc_t rl = make_rsrc(LSEp + (int64_t)bh * S, (uint32_t)S * 4);
+
+  if (nblk == 0) {  // no visible key (L == 0): out = 0, lse = -inf
+    if (wave_live) {
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int ch = tid + j * NT;
-      const int r = ch / CPR, cc = ch - r * CPR;
-      const int key = k0 + r;
-      const bool in = (NCH % NT == 0 || ch < NCH) && key < kend;
-      pk[j] = in ? *(const T8*)(Kh + key * D + cc * 8) : zero_vec<T8>();
-      pv[j] = in ? *(const T8*)(Vh + key * D + cc * 8) : zero_vec<T8>();
+      for (int t = 0; t < NQT; ++t) {
+        const int row = wq0 + 16 * t + c;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) buf_store8(zero_vec<T4>(), ro, (row * D + 16 * dt + 4 * g) * 2);
+        if (LSEp) buf_store4(-INFINITY, rl, g == 0 ? row * 4 : kOutOfRange);
+      }
     }
-  };
-  auto lstore = [&](int st) {
-    T* Ks = smem + st * 2 * TILE;
-    T* Vs = Ks + TILE;
+    return;
+  }
+
+  // ---- per-lane DMA source offsets of this wave's slots (block relative)
+  const rsrc_t rk = make_rsrc(Kp + head, (uint32_t)kend * RB);
+  const rsrc_t rv = make_rsrc(Vp + head, (uint32_t)kend * RB);
+  int koff[NIW], voff[NIW];
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int ch = tid + j * NT;
-      if (NCH % NT == 0 || ch < NCH) {
-        const int r = ch / CPR, cc = ch - r * CPR;
-        *(T8*)(Ks + r * STR + cc * 8) = pk[j];
-        *(T8*)(Vs + r * STR + cc * 8) = pv[j];
+  for (int i = 0; i < NIW; ++i) {
+    const int slot = (wave + i * NW) * 64 + lane;
+    const int row = slot / SPR, j = slot - row * SPR;
+    const bool live = slot < SLOTS && j < D / 8;
+    const int base = 32 * (row >> 5);
+    koff[i] = live ? (base + k_key_of_row(row & 31)) * RB + 16 * j : kOutOfRange;
+    voff[i] = live ? (base + v_key_of_row(row & 31)) * RB + 16 * j : kOutOfRange;
+  }
+  auto dma_block = [&](int st, int k0) {
+    T* Kst = smem + st * 2 * TILE;
+    T* Vst = Kst + TILE;
+#pragma unroll
+    for (int i = 0; i < NIW; ++i) {
+      const int inst = wave + i * NW;
+      if (NI % NW == 0 || inst < NI) {  // wave-uniform
+        dma16(rk, Kst + inst * 512, koff[i], k0 * RB);
+        dma16(rv, Vst + inst * 512, voff[i], k0 * RB);
       }
     }
   };
 
-  if (nblk > 0) gload(0);
+  dma_block(0, 0);
 
+  // ---- Q fragments (rows past S read as zero)
+  const rsrc_t rq = make_rsrc(Qp + head, (uint32_t)S * RB);
   T8 qf[NQT][NKC];
   T4 qf4[NQT];
 #pragma unroll
   for (int t = 0; t < NQT; ++t) {
     const int row = wq0 + 16 * t + c;
     if constexpr (D == 16) {
-      qf4[t] = row < S ? *(const T4*)(Qh + row * D + 4 * g) : zero_vec<T4>();
+      qf4[t] = buf_load8<T4>(rq, (row * D + 4 * g) * 2, 0);
     } else {
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc)
-        qf[t][kc] = row < S ? *(const T8*)(Qh + row * D + 32 * kc + 8 * g) : zero_vec<T8>();
+      for (int kc = 0; kc < NKC; ++kc) qf[t][kc] = buf_load16<T8>(rq, (row * D + 32 * kc + 8 * g) * 2, 0);
     }
   }
 
   float m_run[NQT], l_run[NQT];
-  f32x4 o[NQT][NDT];
+  f32x4 o[NQT][NDT], lsum[NQT];
 #pragma unroll
   for (int t = 0; t < NQT; ++t) {
     m_run[t] = -INFINITY;
     l_run[t] = 0.f;
+    lsum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  T8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = to_t<T>(1.f);
 
-  if (nblk > 0) lstore(0);
-  __syncthreads();
+  // per-lane LDS operand offsets (elements)
+  const int kread = c * STR + 8 * g;  // + (32p + 16h) * STR + 32kc
+  const int kread16 = c * STR + 4 * g;
+  const int vread = (16 * (g >> 1) + 8 * (g & 1) + 2 * (c >> 2)) * STR + 4 * (c & 3);  // + s*STR + 32p*STR + 16dt
 
   for (int kb = 0; kb < nblk; ++kb) {
     const int k0 = kb * BK;
-    const bool more = kb + 1 < nblk;
-    if (more) gload(k0 + BK);  // in flight during this block's arithmetic
+    wait_vmem();      // this wave's copies of block kb have landed
+    __syncthreads();  // ... and everyone's; everyone is done with block kb-1
+    if (kb + 1 < nblk) dma_block((kb + 1) & 1, k0 + BK);  // in flight during this block
+    if (k0 >= kend_w) continue;  // wave-uniform: block is past this wave's rows
 
-    if (k0 < kend_w) {  // wave-uniform: block overlaps this wave's rows
-      const T* Ks = smem + (kb & 1) * 2 * TILE;
-      const T* Vs = Ks + TILE;
+    const T* Ks = smem + (kb & 1) * 2 * TILE;
+    const T* Vs = Ks + TILE;
 
-      // ---- S^T = K Q^T
-      f32x4 s[NQT][NKT];
+    // ---- S^T = K Q^T
+    f32x4 s[NQT][NKT];
 #pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) {
-        const int krow = 32 * (kt >> 1) + 8 * (c >> 2) + 4 * (kt & 1) + (c & 3);
+    for (int kt = 0; kt < NKT; ++kt) {
+      const int rbase = (32 * (kt >> 1) + 16 * (kt & 1)) * STR;
 #pragma unroll
-        for (int t = 0; t < NQT; ++t) s[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (D == 16) {
-          const T4 kf = *(const T4*)(Ks + krow * STR + 4 * g);
+      for (int t = 0; t < NQT; ++t) s[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (D == 16) {
+        const T4 kf = *(const T4*)(Ks + rbase + kread16);
 #pragma unroll
-          for (int t = 0; t < NQT; ++t) s[t][kt] = mfma_k16(kf, qf4[t], s[t][kt]);
-        } else {
+        for (int t = 0; t < NQT; ++t) s[t][kt] = mfma_k16(kf, qf4[t], s[t][kt]);
+      } else {
 #pragma unroll
-          for (int kc = 0; kc < NKC; ++kc) {
-            const T8 kf = *(const T8*)(Ks + krow * STR + 32 * kc + 8 * g);
+        for (int kc = 0; kc < NKC; ++kc) {
+          const T8 kf = *(const T8*)(Ks + rbase + kread + 32 * kc);
 #pragma unroll
-            for (int t = 0; t < NQT; ++t) s[t][kt] = mfma_k32(kf, qf[t][kc], s[t][kt]);
-          }
-        }
-      }
-
-      // ---- mask only blocks that straddle the key length or the diagonal
-      if ((k0 + BK > L) || (causal && (k0 + BK - 1 > wq0))) {
-#pragma unroll
-        for (int t = 0; t < NQT; ++t) {
-          const int row = wq0 + 16 * t + c;
-#pragma unroll
-          for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = k0 + 32 * (kt >> 1) + 8 * g + 4 * (kt & 1) + i;
-              const bool ok = key < L && (!causal || key <= row);
-              s[t][kt][i] = ok ? s[t][kt][i] : -INFINITY;
-            }
-        }
-      }
-
-      // ---- block row maxima; move the running max only when it is exceeded
-      //      by more than the slack (wave-uniform decision)
-      float mb[NQT];
-      bool grow = false;
-#pragma unroll
-      for (int t = 0; t < NQT; ++t) {
-        float mx = s[t][0][0];
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[t][kt][i]);
-        mb[t] = group_max(mx) * c_log2;  // finite: key 0 is visible to every row
-        grow |= mb[t] > m_run[t] + kRescaleSlack;
-      }
-      if (__any(grow)) {
-#pragma unroll
-        for (int t = 0; t < NQT; ++t) {
-          const float m_new = fmaxf(m_run[t], mb[t]);
-          const float alpha = fast_exp2(m_run[t] - m_new);
-          m_run[t] = m_new;
-          l_run[t] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) o[t][dt] *= alpha;
-        }
-      }
-
-      // ---- P = exp2(S c - m); O^T += V^T P^T, one key pair at a time
-#pragma unroll
-      for (int p = 0; p < NKP; ++p) {
-        T8 pf[NQT], pl[NQT];
-#pragma unroll
-        for (int t = 0; t < NQT; ++t) {
-          float ls = 0.f;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float a0 = fast_exp2(fmaf(s[t][2 * p][i], c_log2, -m_run[t]));
-            const float a1 = fast_exp2(fmaf(s[t][2 * p + 1][i], c_log2, -m_run[t]));
-            ls += a0 + a1;
-            pf[t][i] = to_t<T>(a0);
-            pf[t][4 + i] = to_t<T>(a1);
-            if constexpr (kBf16) {
-              pl[t][i] = to_t<T>(a0 - to_f(pf[t][i]));
-              pl[t][4 + i] = to_t<T>(a1 - to_f(pf[t][4 + i]));
-            }
-          }
-          l_run[t] += ls;
-        }
-        const T* vrow = Vs + (32 * p + 8 * g + (c >> 2)) * STR + 4 * (c & 3);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const i16x4 v0 = lds_read_tr16(vrow + 16 * dt);
-          const i16x4 v1 = lds_read_tr16(vrow + 4 * STR + 16 * dt);
-          const T8 vf = __builtin_bit_cast(
-              T8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-          for (int t = 0; t < NQT; ++t) {
-            o[t][dt] = mfma_k32(vf, pf[t], o[t][dt]);
-            if constexpr (kBf16) o[t][dt] = mfma_k32(vf, pl[t], o[t][dt]);
-          }
+          for (int t = 0; t < NQT; ++t) s[t][kt] = mfma_k32(kf, qf[t][kc], s[t][kt]);
         }
       }
     }
 
-    if (more) lstore((kb + 1) & 1);
-    __syncthreads();
+    // ---- mask only blocks that straddle the key length or the diagonal:
+    //      key k0 + 32p + 8g + 4h + i is visible to row r iff key < L and,
+    //      when causal, key <= r
+    if ((k0 + BK > L) || (causal && (k0 + BK - 1 > wq0))) {
+#pragma unroll
+      for (int t = 0; t < NQT; ++t) {
+        const int row = wq0 + 16 * t + c;
+        const int lim = (causal ? min(L - 1, row) : L - 1) - k0 - 8 * g;  // max visible offset
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int off = 32 * (kt >> 1) + 4 * (kt & 1) + i;
+            s[t][kt][i] = off <= lim ? s[t][kt][i] : -INFINITY;
+          }
+      }
+    }
+
+    // ---- block row maxima; move the running max only when it is exceeded
+    //      by more than the slack (wave-uniform decision)
+    float mb[NQT];
+    bool grow = false;
+#pragma unroll
+    for (int t = 0; t < NQT; ++t) {
+      float mx = s[t][0][0];
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[t][kt][i]);
+      mb[t] = group_max(mx) * c_log2;  // finite: key 0 is visible to every row
+      grow |= mb[t] > m_run[t] + kRescaleSlack;
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int t = 0; t < NQT; ++t) {
+        const float m_new = fmaxf(m_run[t], mb[t]);
+        const float alpha = fast_exp2(m_run[t] - m_new);
+        m_run[t] = m_new;
+        l_run[t] *= alpha;
+        lsum[t] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[t][dt] *= alpha;
+      }
+    }
+
+    // ---- P = exp2(S c - m); O^T += V^T P^T, one key pair at a time
+#pragma unroll
+    for (int p = 0; p < NKP; ++p) {
+      T8 pf[NQT], pl[NQT];
+#pragma unroll
+      for (int t = 0; t < NQT; ++t) {
+        float ls = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a0 = fast_exp2(fmaf(s[t][2 * p][i], c_log2, -m_run[t]));
+          const float a1 = fast_exp2(fmaf(s[t][2 * p + 1][i], c_log2, -m_run[t]));
+          if constexpr (!SUM_MFMA) ls += a0 + a1;
+          pf[t][i] = to_t<T>(a0);
+          pf[t][4 + i] = to_t<T>(a1);
+          if constexpr (kBf16) {
+            pl[t][i] = to_t<T>(a0 - to_f(pf[t][i]));
+            pl[t][4 + i] = to_t<T>(a1 - to_f(pf[t][4 + i]));
+          }
+        }
+        if constexpr (SUM_MFMA) {
+          lsum[t] = mfma_k32(ones, pf[t], lsum[t]);
+          if constexpr (kBf16) lsum[t] = mfma_k32(ones, pl[t], lsum[t]);
+        } else {
+          l_run[t] += ls;
+        }
+      }
+      const T* vr = Vs + 32 * p * STR + vread;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const i16x4 v0 = lds_read_tr16(vr + 16 * dt);
+        const i16x4 v1 = lds_read_tr16(vr + STR + 16 * dt);
+        const T8 vf = __builtin_bit_cast(T8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int t = 0; t < NQT; ++t) {
+          o[t][dt] = mfma_k32(vf, pf[t], o[t][dt]);
+          if constexpr (kBf16) o[t][dt] = mfma_k32(vf, pl[t], o[t][dt]);
+        }
+      }
+    }
   }
 
-  // ---- epilogue: O / l rounded once to T; lse = ln(2) * (m + log2 l)
+  // ---- epilogue: O / l rounded once to T; lse = ln(2) * (m + log2 l).
+  //      Rows past S fall outside the store ranges and are dropped.
   if (wave_live) {
 #pragma unroll
     for (int t = 0; t < NQT; ++t) {
-      const float l = group_sum(l_run[t]);
+      const float l = SUM_MFMA ? lsum[t][0] : group_sum(l_run[t]);
       const int row = wq0 + 16 * t + c;
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      if (row < S) {
+      const float inv = 1.f / l;  // l >= 1: the running max's own key contributes 1
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          T4 ov;
+      for (int dt = 0; dt < NDT; ++dt) {
+        T4 ov;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ov[i] = to_t<T>(o[t][dt][i] * inv);
-          *(T4*)(Oh + row * D + 16 * dt + 4 * g) = ov;
-        }
-        if (LSEp && g == 0)
-          LSEp[(int64_t)bh * S + row] = l > 0.f ? (m_run[t] + fast_log2(l)) * kLn2 : -INFINITY;
+        for (int i = 0; i < 4; ++i) ov[i] = to_t<T>(o[t][dt][i] * inv);
+        buf_store8(ov, ro, (row * D + 16 * dt + 4 * g) * 2);
       }
+      if (LSEp) buf_store4((m_run[t] + fast_log2(l)) * kLn2, rl, g == 0 ? row * 4 : kOutOfRange);
     }
   }
 }
 
-template <typename T, int D, int NQT, int NW, int BK>
+template <typename T, int D, int NQT, int NW, int BK, bool SM>
 static hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   constexpr int BQ = NW * NQT * 16;
   const int n_qblk = (p.S + BQ - 1) / BQ;
   const int64_t n_wg = (int64_t)p.B * p.H * n_qblk;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_fwd_mfma<T, D, NQT, NW, BK>), dim3((unsigned)n_wg), dim3(NW * 64), 0, s,
+  hipLaunchKernelGGL((attn_fwd_mfma<T, D, NQT, NW, BK, SM>), dim3((unsigned)n_wg), dim3(NW * 64), 0, s,
                      (const T*)p.q, (const T*)p.k, (const T*)p.v, (T*)p.out, p.lse, p.key_len,
                      p.H, p.S, p.causal, n_qblk, p.c_log2);
   return hipGetLastError();
 }
 
-// Tile shapes (NQT query tiles per wave, NW waves, BK keys per block) per head
-// size. Entry 0 is the default; the others are kept for A/B measurement and
-// are selected with the MHA_TILE_CONFIG environment variable.
+// Tile shapes (NQT query tiles per wave, NW waves, BK keys per block, row sum
+// on the matrix cores) per head size. Entry 0 is the default; the others are
+// kept for A/B measurement and are selected with MHA_TILE_CONFIG.
 template <typename T>
 static hipError_t launch_general(const AttnParams& p, hipStream_t s) {
   const int cfg = p.tile_cfg;
   switch (p.D) {
-    case 16: return launch_one<T, 16, 2, 4, 64>(p, s);
-    case 32: return launch_one<T, 32, 2, 4, 64>(p, s);
+    case 16: return launch_one<T, 16, 2, 4, 64, false>(p, s);
+    case 32: return launch_one<T, 32, 2, 4, 64, false>(p, s);
     case 64:
-      if (cfg == 1) return launch_one<T, 64, 4, 4, 64>(p, s);
-      if (cfg == 2) return launch_one<T, 64, 2, 4, 64>(p, s);
-      if (cfg == 3) return launch_one<T, 64, 2, 8, 128>(p, s);
-      return launch_one<T, 64, 2, 8, 64>(p, s);
+      if (cfg == 1) return launch_one<T, 64, 2, 8, 128, true>(p, s);
+      if (cfg == 2) return launch_one<T, 64, 2, 8, 64, false>(p, s);
+      if (cfg == 3) return launch_one<T, 64, 4, 4, 64, false>(p, s);
+      return launch_one<T, 64, 2, 8, 128, false>(p, s);
     case 128:
-      if (cfg == 1) return launch_one<T, 128, 2, 4, 64>(p, s);
-      return launch_one<T, 128, 2, 8, 64>(p, s);
+      if (cfg == 1) return launch_one<T, 128, 2, 4, 64, false>(p, s);
+      return launch_one<T, 128, 2, 8, 64, false>(p, s);
     case 256:
-      if (cfg == 1) return launch_one<T, 256, 1, 8, 32>(p, s);
-      if (cfg == 2) return launch_one<T, 256, 2, 8, 32>(p, s);
-      if (cfg == 3) return launch_one<T, 256, 1, 4, 64>(p, s);
-      return launch_one<T, 256, 2, 4, 32>(p, s);
+      if (cfg == 1) return launch_one<T, 256, 1, 8, 32, false>(p, s);
+      if (cfg == 2) return launch_one<T, 256, 2, 8, 32, true>(p, s);
+      if (cfg == 3) return launch_one<T, 256, 2, 4, 32, false>(p, s);
+      return launch_one<T, 256, 2, 8, 32, false>(p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -310,11 +352,11 @@ static hipError_t launch_general(const AttnParams& p, hipStream_t s) {
 template <typename T>
 static hipError_t launch_small(const AttnParams& p, hipStream_t s) {
   switch (p.D) {
-    case 16: return launch_one<T, 16, 1, 1, 64>(p, s);
-    case 32: return launch_one<T, 32, 1, 1, 64>(p, s);
-    case 64: return launch_one<T, 64, 1, 1, 64>(p, s);
-    case 128: return launch_one<T, 128, 1, 1, 64>(p, s);
-    case 256: return launch_one<T, 256, 1, 1, 32>(p, s);
+    case 16: return launch_one<T, 16, 1, 1, 64, false>(p, s);
+    case 32: return launch_one<T, 32, 1, 1, 64, false>(p, s);
+    case 64: return launch_one<T, 64, 1, 1, 64, false>(p, s);
+    case 128: return launch_one<T, 128, 1, 1, 64, false>(p, s);
+    case 256: return launch_one<T, 256, 1, 1, 32, false>(p, s);
   }
   return hipErrorInvalidValue;
 }

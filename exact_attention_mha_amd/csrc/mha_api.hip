@@ -39,7 +39,8 @@ int validate(const void* q, const void* k, const void* v, void* out, const float
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
     return MHA_ERR_MISALIGNED;
   if ((lse && !aligned(lse, 4)) || (key_len && !aligned(key_len, 4))) return MHA_ERR_MISALIGNED;
-  if (S * d_h >= (int64_t)1 << 31) return MHA_ERR_SHAPE;  // per-head offsets are 32-bit
+  const int64_t esize = dtype == MHA_F32 ? 4 : 2;
+  if (S * d_h * esize >= (int64_t)1 << 31) return MHA_ERR_SHAPE;  // per-head byte offsets are 32-bit
   if (B * H >= (int64_t)1 << 31) return MHA_ERR_SHAPE;
   return MHA_OK;
 }

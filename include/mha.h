@@ -45,8 +45,8 @@ enum mha_dtype {
 enum mha_status {
   MHA_OK = 0,
   MHA_ERR_NULL = 1,        /* a required pointer is NULL */
-  MHA_ERR_SHAPE = 2,       /* negative size, or sizes beyond the 32-bit
-                              per-head / grid limits stated below */
+  MHA_ERR_SHAPE = 2,       /* negative size, or sizes beyond the per-head
+                              byte / grid limits stated below */
   MHA_ERR_UNSUPPORTED = 3, /* d_h or dtype or variant not supported */
   MHA_ERR_MISALIGNED = 4,  /* q/k/v/out not 16-byte aligned, lse/key_len not
                               4-byte aligned */
@@ -80,8 +80,9 @@ enum mha_variant {
  *            written). lse[b,h,i] = ln(sum over visible j of
  *            exp(q_i . k_j / sqrt(d_h))), -inf for rows with no visible key.
  *   B, H, S  batch, heads, sequence length (>= 0; any of them 0 is a no-op
- *            returning MHA_OK). S * d_h must be < 2^31 and the launch must
- *            fit a 2^31-1 workgroup grid.
+ *            returning MHA_OK). One head must span fewer than 2^31 bytes
+ *            (S * d_h * element size < 2^31) and the launch must fit a
+ *            2^31-1 workgroup grid.
  *   d_h      head dimension: 16, 32, 64, 128 or 256.
  *   causal   non-zero: key j visible to row i only if j <= i.
  *   key_len  device pointer to int32[B] or NULL (all S keys valid). Values

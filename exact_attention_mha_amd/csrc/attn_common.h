@@ -100,21 +100,59 @@ __device__ __forceinline__ void dma16(rsrc_t r, void* lds, int voff, int soff) {
 }
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left unconstrained)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// s_waitcnt vmcnt(N): at most N (the most recent) vector-memory operations
+// still outstanding; vmcnt occupies bits [3:0] and [15:14] of the gfx9
+// s_waitcnt immediate
+template <int N>
+__device__ __forceinline__ void wait_vmem_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
 
 // ---- transcendental helpers (single hardware instructions) ----------------
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// ---- cross-group reductions: lanes c, c+16, c+32, c+48 share a query ------
-__device__ __forceinline__ float group_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+// max(a, b, c) as one v_max3_f32. Operands are never NaN here (masked scores
+// are -inf), so the quieting moves the compiler adds around fmaxf are not
+// needed.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
+
+__device__ __forceinline__ float max2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// Workgroup barrier without the release fence of __syncthreads (which would
+// drain every outstanding global->LDS copy). Callers order their own copies
+// with an explicit vmcnt wait before it; the memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// ---- cross-group reductions: lanes c, c+16, c+32, c+48 share a query ------
+// v_permlane16_swap(x, x) yields, in its two results, the values of lanes
+// i and i^16 (in some order) at every lane i; v_permlane32_swap likewise for
+// i and i^32. Combining the pair reduces over the four lane groups on the
+// vector ALU, with no LDS round trip.
+__device__ __forceinline__ float xor16_pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float group_max(float x) { return xor32_pair_max(xor16_pair_max(x)); }
 __device__ __forceinline__ float group_sum(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // ---- conversions -------------------------------------------------------------

@@ -52,7 +52,7 @@ __device__ __forceinline__ int v_key_of_row(int rho) {
   return 16 * (rho >> 4) + 8 * ((rho >> 3) & 1) + 4 * (rho & 1) + ((rho >> 1) & 3);
 }
 
-template <typename T, int D, int NQT, int NW, int BK, bool SUM_MFMA>
+template <typename T, int D, int NQT, int NW, int BK, bool SUM_MFMA, int NST>
 __global__ void __launch_bounds__(NW * 64)
 attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
               T* __restrict__ Op, float* __restrict__ LSEp, const int32_t* __restrict__ key_len,
@@ -74,10 +74,11 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   constexpr bool kBf16 = __is_same(T, bf16_t);
   static_assert(BK % 32 == 0 && D % 16 == 0, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) T smem[2 * 2 * TILE];  // [stage][K, V]
+  __shared__ __attribute__((aligned(16))) T smem[NST * 2 * TILE];  // [stage][K, V]
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
 
   const uint32_t logical = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -138,8 +139,6 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
     }
   };
 
-  dma_block(0, 0);
-
   // ---- Q fragments (rows past S read as zero)
   const rsrc_t rq = make_rsrc(Qp + head, (uint32_t)S * RB);
   T8 qf[NQT][NKC];
@@ -152,6 +151,26 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
     } else {
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) qf[t][kc] = buf_load16<T8>(rq, (row * D + 32 * kc + 8 * g) * 2, 0);
+    }
+  }
+
+  asm volatile("" ::: "memory");  // Q loads are issued (and so retire) before the copies
+  // prologue copies; unconditional (blocks past the visible keys read as
+  // zero) so the outstanding count below is fixed
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st) dma_block(st, st * BK);
+  // the Q loads are older than every copy: this retires them before the loop
+  wait_vmem_keep<2 * (NI / NW) * (NST - 1)>();
+  // and this tells the compiler so: the fragments' last definition is now an
+  // (empty) register-only instruction, not a pending load, so it adds no
+  // load waits inside the loop
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    if constexpr (D == 16) {
+      asm volatile("" : "+v"(qf4[t]));
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) asm volatile("" : "+v"(qf[t][kc]));
     }
   }
 
@@ -176,12 +195,16 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
 
   for (int kb = 0; kb < nblk; ++kb) {
     const int k0 = kb * BK;
-    wait_vmem();      // this wave's copies of block kb have landed
-    __syncthreads();  // ... and everyone's; everyone is done with block kb-1
-    if (kb + 1 < nblk) dma_block((kb + 1) & 1, k0 + BK);  // in flight during this block
+    // this wave's copies of block kb have landed (later blocks may still be
+    // in flight); after the barrier everyone's have, and everyone is done
+    // with block kb-1, whose stage the next copy reuses
+    if (NST == 2 || kb + 1 >= nblk) wait_vmem();
+    else wait_vmem_keep<2 * (NI / NW) * (NST - 2)>();  // every wave issues >= NI/NW per tile
+    block_barrier();
+    if (kb + NST - 1 < nblk) dma_block((kb + NST - 1) % NST, k0 + (NST - 1) * BK);
     if (k0 >= kend_w) continue;  // wave-uniform: block is past this wave's rows
 
-    const T* Ks = smem + (kb & 1) * 2 * TILE;
+    const T* Ks = smem + (kb % NST) * 2 * TILE;
     const T* Vs = Ks + TILE;
 
     // ---- S^T = K Q^T
@@ -231,9 +254,10 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
     for (int t = 0; t < NQT; ++t) {
       float mx = s[t][0][0];
 #pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[t][kt][i]);
+      for (int kt = 0; kt < NKT; ++kt) {
+        mx = max3(mx, s[t][kt][0], s[t][kt][1]);
+        mx = max3(mx, s[t][kt][2], s[t][kt][3]);
+      }
       mb[t] = group_max(mx) * c_log2;  // finite: key 0 is visible to every row
       grow |= mb[t] > m_run[t] + kRescaleSlack;
     }
@@ -311,13 +335,13 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   }
 }
 
-template <typename T, int D, int NQT, int NW, int BK, bool SM>
+template <typename T, int D, int NQT, int NW, int BK, bool SM, int NST = 2>
 static hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   constexpr int BQ = NW * NQT * 16;
   const int n_qblk = (p.S + BQ - 1) / BQ;
   const int64_t n_wg = (int64_t)p.B * p.H * n_qblk;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_fwd_mfma<T, D, NQT, NW, BK, SM>), dim3((unsigned)n_wg), dim3(NW * 64), 0, s,
+  hipLaunchKernelGGL((attn_fwd_mfma<T, D, NQT, NW, BK, SM, NST>), dim3((unsigned)n_wg), dim3(NW * 64), 0, s,
                      (const T*)p.q, (const T*)p.k, (const T*)p.v, (T*)p.out, p.lse, p.key_len,
                      p.H, p.S, p.causal, n_qblk, p.c_log2);
   return hipGetLastError();
@@ -334,17 +358,17 @@ static hipError_t launch_general(const AttnParams& p, hipStream_t s) {
     case 32: return launch_one<T, 32, 2, 4, 64, false>(p, s);
     case 64:
       if (cfg == 1) return launch_one<T, 64, 2, 8, 128, true>(p, s);
-      if (cfg == 2) return launch_one<T, 64, 2, 8, 64, false>(p, s);
-      if (cfg == 3) return launch_one<T, 64, 4, 4, 64, false>(p, s);
-      return launch_one<T, 64, 2, 8, 128, false>(p, s);
+      if (cfg == 2) return launch_one<T, 64, 2, 8, 64, true, 3>(p, s);
+      if (cfg == 3) return launch_one<T, 64, 2, 8, 64, false>(p, s);
+      return launch_one<T, 64, 2, 8, 64, true>(p, s);
     case 128:
-      if (cfg == 1) return launch_one<T, 128, 2, 4, 64, false>(p, s);
-      return launch_one<T, 128, 2, 8, 64, false>(p, s);
+      if (cfg == 1) return launch_one<T, 128, 2, 8, 64, true, 3>(p, s);
+      return launch_one<T, 128, 2, 8, 64, true>(p, s);
     case 256:
-      if (cfg == 1) return launch_one<T, 256, 1, 8, 32, false>(p, s);
-      if (cfg == 2) return launch_one<T, 256, 2, 8, 32, true>(p, s);
-      if (cfg == 3) return launch_one<T, 256, 2, 4, 32, false>(p, s);
-      return launch_one<T, 256, 2, 8, 32, false>(p, s);
+      if (cfg == 1) return launch_one<T, 256, 2, 8, 32, true, 3>(p, s);
+      if (cfg == 2) return launch_one<T, 256, 2, 8, 32, true, 4>(p, s);
+      if (cfg == 3) return launch_one<T, 256, 2, 8, 32, false>(p, s);
+      return launch_one<T, 256, 2, 8, 32, true>(p, s);
   }
   return hipErrorInvalidValue;
 }

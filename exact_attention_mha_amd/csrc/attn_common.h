@@ -35,6 +35,8 @@ template <typename T> struct Vec;
 template <> struct Vec<f16_t> { typedef f16x8 x8; typedef f16x4 x4; };
 template <> struct Vec<bf16_t> { typedef bf16x8 x8; typedef bf16x4 x4; };
 
+template <typename V> __device__ __forceinline__ V zero_vec();
+
 // ---- matrix-core products (fp32 accumulate) ---------------------------------
 __device__ __forceinline__ f32x4 mfma_k32(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -45,9 +47,13 @@ __device__ __forceinline__ f32x4 mfma_k32(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma_k16(f16x4 a, f16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
+// bf16 K=16 products go through the K=32 instruction with the upper half of
+// both operands zero (the same sum: zero products add nothing), so fp16 and
+// bf16 use the same two instruction shapes.
 __device__ __forceinline__ f32x4 mfma_k16(bf16x4 a, bf16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
-                                                   __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+  const bf16x8 a8 = __builtin_shufflevector(a, zero_vec<bf16x4>(), 0, 1, 2, 3, 4, 5, 6, 7);
+  const bf16x8 b8 = __builtin_shufflevector(b, zero_vec<bf16x4>(), 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);

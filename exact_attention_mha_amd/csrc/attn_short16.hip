@@ -1,0 +1,199 @@
+// Short-sequence attention forward for d_h = 16 heads (S <= 128), fp16/bf16.
+//
+// The regime of many tiny heads (the bandwidth-bound shape: tens of thousands
+// of heads of 128 rows x 16 columns) is decided by per-head overhead, so this
+// kernel has none to spare: one wave owns one head (or, for launch-bound
+// shapes with few heads, a balanced pair of 16-row query tiles of a head),
+// there is no LDS and no barrier, and every operand is loaded straight from
+// memory in the layout the matrix cores consume:
+//   * K rows and Q rows are the A / B operands of S^T = K Q^T
+//     (16x16x16 MFMA): lane (g, c) reads 8 bytes, row c, columns 4g..4g+3;
+//     16 lanes cover 512 contiguous bytes.
+//   * V is read the same way and transposed by one 16x16x16 MFMA against an
+//     identity operand (exact: every product is v * 1 or v * 0), which leaves
+//     V^T in the A-operand layout of O^T += V^T P^T.
+// A whole score row fits in registers, so each query tile takes a single
+// pass: row maximum, exponentials, P.V, no rescaling (devpost
+// "gpu-transformer-optimization", section 2.2: at S <= 128 the score row
+// fits at once and no online softmax is needed). Only key tiles a query tile
+// can see are computed: up to its own diagonal when causal, never past the
+// key length. The row sum comes from a ones operand times the same rounded P
+// as the numerator. Rows past S and keys past the key length are handled by
+// the buffer range checks (reads as zero, stores dropped).
+#include <utility>
+
+#include "attn_common.h"
+#include "launch.h"
+
+namespace mha {
+
+template <typename T, int QPW, bool CAUSAL>
+__global__ void __launch_bounds__(256)
+attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
+                 T* __restrict__ Op, float* __restrict__ LSEp, const int32_t* __restrict__ key_len,
+                 int BH, int H, int S, float c_log2) {
+  constexpr bool causal = CAUSAL;
+  typedef typename Vec<T>::x4 T4;
+  constexpr int D = 16;
+  constexpr int RB = D * (int)sizeof(T);  // 32 bytes per row
+  constexpr int NT = 8;                    // 16-row tiles in S <= 128
+  constexpr int PARTS = NT / QPW;          // waves per head
+  constexpr bool kBf16 = __is_same(T, bf16_t);
+  static_assert(QPW == 8 || QPW == 2, "whole head or a balanced tile pair per wave");
+
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int item = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
+  const int bh = item / PARTS, part = item - bh * PARTS;
+  if (bh >= BH) return;  // wave-uniform; no barriers in this kernel
+  const int b = bh / H;
+  const int L = clamp_len(key_len, b, S);
+  const int64_t head = (int64_t)bh * S * D;
+  const rsrc_t rq = make_rsrc(Qp + head, (uint32_t)S * RB);
+  const rsrc_t rk = make_rsrc(Kp + head, (uint32_t)L * RB);
+  const rsrc_t rv = make_rsrc(Vp + head, (uint32_t)L * RB);
+  const rsrc_t ro = make_rsrc(Op + head, (uint32_t)S * RB);
+  const rsrc_t rl = make_rsrc(LSEp + (int64_t)bh * S, (uint32_t)S * 4);
+
+  // query tiles of this wave; with pairs, wave `part` takes tiles part and
+  // 7-part, so every wave of a causal head does 9 key tiles of work
+  int tile[QPW];
+#pragma unroll
+  for (int j = 0; j < QPW; ++j) tile[j] = QPW == NT ? j : (j == 0 ? part : NT - 1 - part);
+  int kt_need = NT;  // key tiles the computation touches (past L they read zero)
+  if (causal) {
+    int tmax = 0;
+#pragma unroll
+    for (int j = 0; j < QPW; ++j) tmax = max(tmax, tile[j]);
+    kt_need = tmax + 1;
+  }
+
+  // ---- operands straight from memory (keys past L and rows past S read 0)
+  T4 qf[QPW], kf[NT], vt[NT];
+#pragma unroll
+  for (int j = 0; j < QPW; ++j) qf[j] = buf_load8<T4>(rq, (16 * tile[j] + c) * RB + 8 * g, 0);
+  T4 vraw[NT];
+#pragma unroll
+  for (int kt = 0; kt < NT; ++kt) {
+    if (kt < kt_need) {
+      kf[kt] = buf_load8<T4>(rk, (16 * kt + c) * RB + 8 * g, 0);
+      vraw[kt] = buf_load8<T4>(rv, (16 * kt + c) * RB + 8 * g, 0);
+    }
+  }
+  T4 ident, ones;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    ident[e] = to_t<T>(4 * g + e == c ? 1.f : 0.f);
+    ones[e] = to_t<T>(1.f);
+  }
+#pragma unroll
+  for (int kt = 0; kt < NT; ++kt) {
+    if (kt < kt_need) {
+      const f32x4 d = mfma_k16(vraw[kt], ident, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vt[kt][e] = to_t<T>(d[e]);  // exact: d holds V values
+    }
+  }
+
+  // Masks ride in the S^T accumulator: each product starts from a bias tile
+  // of 0 (visible) or -inf (hidden), so hidden scores come out as -inf with
+  // no per-element work. Register i of lane (g, c) in key tile kt is key
+  // 16kt + 4g + i of row 16t + c. bias[kt] encodes the key length; the
+  // causal diagonal adds key <= row on tile t only.
+  f32x4 bias[NT], diag;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int kt = 0; kt < NT; ++kt) bias[kt][i] = 16 * kt + 4 * g + i < L ? 0.f : -INFINITY;
+    diag[i] = 4 * g + i <= c ? 0.f : -INFINITY;
+  }
+
+  // one query tile, with its index a compile-time constant so that every
+  // register array is indexed statically; every key tile up to the diagonal
+  // (causal) or all of them is computed without branches
+  auto qtile = [&](auto J) {
+    constexpr int j = decltype(J)::value;
+    const int t = tile[j];
+    if (16 * t >= S) return;  // wave-uniform
+    const int row = 16 * t + c;
+    if (L == 0) {  // no visible key
+      buf_store8(zero_vec<T4>(), ro, row * RB + 8 * g);
+      if (LSEp) buf_store4(-INFINITY, rl, g == 0 ? row * 4 : kOutOfRange);
+      return;
+    }
+    constexpr int NK = (QPW == NT && CAUSAL) ? j + 1 : NT;  // key tiles computed
+    f32x4 s[NT];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < NK; ++kt) {
+      if (CAUSAL && QPW != NT && kt > t) break;  // split waves: tile index is runtime
+      f32x4 init = bias[kt];
+      if (CAUSAL && kt == t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) init[i] = fminf(init[i], diag[i]);
+      }
+      s[kt] = mfma_k16(kf[kt], qf[j], init);
+      mx = max3(mx, s[kt][0], s[kt][1]);
+      mx = max3(mx, s[kt][2], s[kt][3]);
+    }
+    const float m = group_max(mx) * c_log2;  // finite: key 0 is visible
+    f32x4 o = {0.f, 0.f, 0.f, 0.f}, lsum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < NK; ++kt) {
+      if (CAUSAL && QPW != NT && kt > t) break;
+      T4 pf, pl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = fast_exp2(fmaf(s[kt][i], c_log2, -m));
+        pf[i] = to_t<T>(pv);
+        if constexpr (kBf16) pl[i] = to_t<T>(pv - to_f(pf[i]));
+      }
+      o = mfma_k16(vt[kt], pf, o);
+      lsum = mfma_k16(ones, pf, lsum);
+      if constexpr (kBf16) {
+        o = mfma_k16(vt[kt], pl, o);
+        lsum = mfma_k16(ones, pl, lsum);
+      }
+    }
+    const float l = lsum[0];  // every row of the ones product holds the full sum
+    const float inv = 1.f / l;
+    T4 ov;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ov[i] = to_t<T>(o[i] * inv);
+    buf_store8(ov, ro, row * RB + 8 * g);  // O^T lane layout: row, columns 4g..4g+3
+    if (LSEp) buf_store4((m + fast_log2(l)) * kLn2, rl, g == 0 ? row * 4 : kOutOfRange);
+    __builtin_amdgcn_sched_barrier(0);  // keep query tiles from interleaving (register pressure)
+  };
+  [&]<int... J>(std::integer_sequence<int, J...>) {
+    (qtile(std::integral_constant<int, J>{}), ...);
+  }(std::make_integer_sequence<int, QPW>{});
+}
+
+template <typename T, int QPW>
+static hipError_t launch_one_short16(const AttnParams& p, hipStream_t s) {
+  constexpr int PARTS = 8 / QPW;
+  const int64_t waves = (int64_t)p.B * p.H * PARTS;
+  const int64_t n_wg = (waves + 3) / 4;
+  if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (p.causal)
+    hipLaunchKernelGGL((attn_fwd_short16<T, QPW, true>), dim3((unsigned)n_wg), dim3(256), 0, s,
+                       (const T*)p.q, (const T*)p.k, (const T*)p.v, (T*)p.out, p.lse, p.key_len,
+                       p.B * p.H, p.H, p.S, p.c_log2);
+  else
+    hipLaunchKernelGGL((attn_fwd_short16<T, QPW, false>), dim3((unsigned)n_wg), dim3(256), 0, s,
+                       (const T*)p.q, (const T*)p.k, (const T*)p.v, (T*)p.out, p.lse, p.key_len,
+                       p.B * p.H, p.H, p.S, p.c_log2);
+  return hipGetLastError();
+}
+
+// Few heads (launch-bound): split each head over 4 waves (balanced tile
+// pairs); many heads: one wave per head.
+hipError_t launch_short16(const AttnParams& p, hipStream_t s) {
+  if (p.D != 16 || p.S > 128) return hipErrorInvalidValue;
+  const bool split = (int64_t)p.B * p.H < 2048;
+  if (p.dtype == 1) return split ? launch_one_short16<f16_t, 2>(p, s) : launch_one_short16<f16_t, 8>(p, s);
+  if (p.dtype == 2) return split ? launch_one_short16<bf16_t, 2>(p, s) : launch_one_short16<bf16_t, 8>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mha

@@ -28,6 +28,7 @@ hipError_t launch_mfma(const AttnParams& p, hipStream_t s);        // general ti
 hipError_t launch_mfma_small(const AttnParams& p, hipStream_t s);  // few rows per WG
 hipError_t launch_f32(const AttnParams& p, hipStream_t s);         // fp32 inputs
 hipError_t launch_valu_d16(const AttnParams& p, hipStream_t s);    // d_h = 16 VALU
-hipError_t launch_short(const AttnParams& p, hipStream_t s);       // S <= 128 one pass
+hipError_t launch_short(const AttnParams& p, hipStream_t s);       // S <= 128 one pass, d_h 32/64
+hipError_t launch_short16(const AttnParams& p, hipStream_t s);     // S <= 128 one pass, d_h 16
 
 }  // namespace mha

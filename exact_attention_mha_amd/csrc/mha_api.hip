@@ -16,6 +16,9 @@ bool supported_d(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128 |
 
 // Static kernel choice by regime (dtype, d_h, sequence length, head count):
 //  * fp32 inputs                         -> fp32 matrix-core kernel
+//  * S <= 128 and d_h == 16              -> one pass per head, no LDS (any
+//                                           head count: few heads are split
+//                                           over four waves each)
 //  * S <= 128 and d_h <= 64, many heads  -> one pass per head, no rescaling
 //  * few heads (fewer than ~2 workgroups per CU with 128-row tiles)
 //                                        -> 16-row tiles, one wave each
@@ -23,6 +26,7 @@ bool supported_d(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128 |
 int choose(int64_t B, int64_t H, int64_t S, int64_t D, int dtype) {
   if (dtype == MHA_F32) return MHA_VARIANT_F32;
   const int64_t heads = B * H;
+  if (S <= 128 && D == 16) return MHA_VARIANT_SHORT;
   if (S <= 128 && D <= 64 && heads >= 512) return MHA_VARIANT_SHORT;
   const int64_t wg128 = heads * ((S + 127) / 128);
   if (wg128 < 512) return MHA_VARIANT_MFMA_SMALL;
@@ -103,7 +107,7 @@ int mha_forward_variant(const void* q, const void* k, const void* v, void* out, 
     case MHA_VARIANT_MFMA: e = mha::launch_mfma(p, s); break;
     case MHA_VARIANT_MFMA_SMALL: e = mha::launch_mfma_small(p, s); break;
     case MHA_VARIANT_VALU_D16: e = mha::launch_valu_d16(p, s); break;
-    case MHA_VARIANT_SHORT: e = mha::launch_short(p, s); break;
+    case MHA_VARIANT_SHORT: e = d_h == 16 ? mha::launch_short16(p, s) : mha::launch_short(p, s); break;
   }
   if (e == hipErrorInvalidConfiguration) return MHA_ERR_SHAPE;
   return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;

@@ -82,7 +82,8 @@ def test_variant_selection(mha):
     import torch
     sel = mha.select_variant
     assert sel(1, 2, 64, 32, False, torch.float32) == "f32"
-    assert sel(1, 8, 128, 16, True, torch.float16) == "mfma_small"
+    assert sel(1, 8, 128, 16, True, torch.float16) == "short"
+    assert sel(1, 8, 512, 64, True, torch.float16) == "mfma_small"
     assert sel(10000, 8, 128, 16, True, torch.float16) == "short"
     assert sel(16, 4, 1024, 256, False, torch.float16) == "mfma"
     assert sel(32, 16, 100000, 64, True, torch.float16) == "mfma"

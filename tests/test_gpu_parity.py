@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import check_full, check_rows, run_gpu, workload_case, THREADS
+from gpu_helpers import check_full, check_rows, run_gpu, to_dev, workload_case, THREADS
 from workloads import WORKLOADS, make_inputs, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -180,3 +180,37 @@ def test_without_lse_and_on_a_side_stream(mha):
     assert lse is None
     ro, _ = oracle.attention(q.cpu(), k.cpu(), v.cpu())
     assert oracle.gate(out.cpu(), ro).all()
+
+
+@pytest.mark.parametrize("wl,variant", [("launch", "auto"), ("launch", "mfma_small"),
+                                        ("compute", "auto")])
+def test_graph_replays_match_eager(mha, wl, variant):
+    """The forward captured in a HIP graph (as the launch-bound benchmark
+    replays it) gives, on every replay, exactly the eager result; eager work
+    and synchronisations run between the replays, and the inputs change in
+    place between replays so that a replay cannot pass on stale outputs."""
+    w = WORKLOADS[wl].with_(B=min(WORKLOADS[wl].B, 2))
+    q, k, v, kl = to_dev(*make_inputs(w, 11))
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            mha.forward(q, k, v, causal=w.causal, key_len=kl, out=out, lse=lse,
+                        variant=variant, stream=cap)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    for rep in range(4):
+        if rep:
+            q.copy_(torch.randn(q.shape, generator=gen, device="cuda").to(q.dtype))
+        ref_o, ref_l = mha.forward(q, k, v, causal=w.causal, key_len=kl, variant=variant)
+        torch.cuda.synchronize()
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {rep}"
+    check_full(out.cpu(), lse.cpu(), q.cpu(), k.cpu(), v.cpu(),
+               None if kl is None else kl.cpu(), w.causal, f"graph {wl} {variant}")

@@ -23,10 +23,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
-# (Forcing the VGPR form of the matrix-core instructions with
-# -mllvm -amdgpu-mfma-vgpr-form produced wrong results on gfx950 in the
-# short-sequence kernel -- stale reads of matrix-core results -- so the
-# compiler's own choice of result registers is kept.)
+# Where matrix-core results land (ordinary VGPRs or accumulation registers)
+# is left to the compiler; kernels steer it with their launch bounds.
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

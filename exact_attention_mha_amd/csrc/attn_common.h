@@ -15,6 +15,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <utility>
 #include <stdint.h>
 
 namespace mha {
@@ -69,6 +71,44 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
       (__attribute__((address_space(3))) i16x4*)(p));
 }
 
+// The same read issued through inline asm at LDS byte address addr + OFF.
+// The compiler makes every LDS read it can see wait for all buffer->LDS
+// copies in flight (s_waitcnt vmcnt(0)), including copies of later blocks
+// into another stage, which would pull the copy latency into every block.
+// It cannot see this one, so it adds no such wait -- and no wait for the
+// result either: the caller orders each result with lgkm_wait<N>() before its
+// first use. The caller also guarantees, by its own waits and barriers, that
+// the copy which wrote the bytes read here has completed.
+template <int OFF>
+__device__ __forceinline__ i16x4 lds_read_tr16_asm(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  i16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+// s_waitcnt lgkmcnt(N): at most N LDS operations still outstanding. LDS
+// operations complete in issue order, so the reads issued before the last N
+// have landed. The two fragments pass through the instruction, which ties
+// their uses to the wait.
+template <int N>
+__device__ __forceinline__ void lgkm_wait(i16x4& a, i16x4& b) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1, so that loop
+// indices are compile-time constants (static register indexing, immediate
+// instruction offsets).
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+  }(std::make_integer_sequence<int, N>{});
+}
+
 // ---- buffer addressing -------------------------------------------------------
 // Raw buffer resources carry a byte range; loads past it return zero without
 // touching memory and stores past it are dropped. Kernels use this as the
@@ -119,15 +159,17 @@ __device__ __forceinline__ void wait_vmem_keep() {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// max(a, b, c) as one v_max3_f32. Operands are never NaN here (masked scores
-// are -inf), so the quieting moves the compiler adds around fmaxf are not
-// needed.
-__device__ __forceinline__ float max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
+// max(a, b, c). Its operands are often fresh matrix-core results, and a
+// vector-ALU read of one needs wait states after the producing instruction
+// that only the compiler inserts (it does not look inside inline asm), so
+// this stays plain code; the compiler still forms one v_max3_f32 per call,
+// plus a quieting move at the head of a chain.
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
+// max(a, b) as one v_max_f32, without the quieting moves the compiler puts
+// around fmaxf. Only for operands produced by ordinary vector-ALU
+// instructions (the lane permutes below), never straight from a matrix-core
+// result. Operands are never NaN here (masked scores are -inf).
 __device__ __forceinline__ float max2(float a, float b) {
   float r;
   asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));

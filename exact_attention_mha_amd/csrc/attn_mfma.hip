@@ -198,8 +198,12 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
     // this wave's copies of block kb have landed (later blocks may still be
     // in flight); after the barrier everyone's have, and everyone is done
     // with block kb-1, whose stage the next copy reuses
-    if (NST == 2 || kb + 1 >= nblk) wait_vmem();
-    else wait_vmem_keep<2 * (NI / NW) * (NST - 2)>();  // every wave issues >= NI/NW per tile
+    // With NST - 2 later blocks issued, those may stay in flight (every wave
+    // issues at least NI/NW copies per tile, so keeping that many per tile
+    // outstanding never leaves one of block kb's); near the end fewer later
+    // blocks exist and everything is waited for.
+    if (NST == 2 || kb + NST - 2 >= nblk) wait_vmem();
+    else wait_vmem_keep<2 * (NI / NW) * (NST - 2)>();
     block_barrier();
     if (kb + NST - 1 < nblk) dma_block((kb + NST - 1) % NST, k0 + (NST - 1) * BK);
     if (k0 >= kend_w) continue;  // wave-uniform: block is past this wave's rows
@@ -274,9 +278,11 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
       }
     }
 
-    // ---- P = exp2(S c - m); O^T += V^T P^T, one key pair at a time
-#pragma unroll
-    for (int p = 0; p < NKP; ++p) {
+    // ---- P = exp2(S c - m); O^T += V^T P^T, one key pair at a time. The
+    //      V^T fragments are read LA column tiles ahead of their products.
+    const uint32_t vaddr = lds_addr(Vs + vread);
+    static_for<NKP>([&](auto P) {
+      constexpr int p = decltype(P)::value;
       T8 pf[NQT], pl[NQT];
 #pragma unroll
       for (int t = 0; t < NQT; ++t) {
@@ -300,19 +306,27 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
           l_run[t] += ls;
         }
       }
-      const T* vr = Vs + 32 * p * STR + vread;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const i16x4 v0 = lds_read_tr16(vr + 16 * dt);
-        const i16x4 v1 = lds_read_tr16(vr + STR + 16 * dt);
-        const T8 vf = __builtin_bit_cast(T8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      constexpr int LA = NDT < 4 ? NDT : 4;
+      i16x4 va[NDT], vb[NDT];
+      auto issue = [&](auto J) {
+        constexpr int j = decltype(J)::value;
+        va[j] = lds_read_tr16_asm<(32 * p * STR + 16 * j) * (int)sizeof(T)>(vaddr);
+        vb[j] = lds_read_tr16_asm<((32 * p + 1) * STR + 16 * j) * (int)sizeof(T)>(vaddr);
+      };
+      static_for<LA>(issue);
+      static_for<NDT>([&](auto DT) {
+        constexpr int dt = decltype(DT)::value;
+        if constexpr (dt + LA < NDT) issue(std::integral_constant<int, dt + LA>{});
+        constexpr int last = dt + LA < NDT ? dt + LA : NDT - 1;
+        lgkm_wait<2 * (last - dt)>(va[dt], vb[dt]);  // reads issued after this tile's
+        const T8 vf = __builtin_bit_cast(T8, __builtin_shufflevector(va[dt], vb[dt], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int t = 0; t < NQT; ++t) {
           o[t][dt] = mfma_k32(vf, pf[t], o[t][dt]);
           if constexpr (kBf16) o[t][dt] = mfma_k32(vf, pl[t], o[t][dt]);
         }
-      }
-    }
+      });
+    });
   }
 
   // ---- epilogue: O / l rounded once to T; lse = ln(2) * (m + log2 l).

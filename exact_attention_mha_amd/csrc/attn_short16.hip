@@ -27,8 +27,11 @@
 
 namespace mha {
 
+// At least two waves per SIMD: with that budget (<= 256 registers per lane)
+// the compiler keeps matrix-core results in ordinary VGPRs, where the softmax
+// reads them, instead of accumulation registers that need a copy per value.
 template <typename T, int QPW, bool CAUSAL>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 2)
 attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
                  T* __restrict__ Op, float* __restrict__ LSEp, const int32_t* __restrict__ key_len,
                  int BH, int H, int S, float c_log2) {
@@ -60,12 +63,14 @@ attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __
   int tile[QPW];
 #pragma unroll
   for (int j = 0; j < QPW; ++j) tile[j] = QPW == NT ? j : (j == 0 ? part : NT - 1 - part);
-  int kt_need = NT;  // key tiles the computation touches (past L they read zero)
+  // key tiles the computation touches: none past the key length, none past
+  // the last diagonal when causal
+  int kt_need = (L + 15) >> 4;
   if (causal) {
     int tmax = 0;
 #pragma unroll
     for (int j = 0; j < QPW; ++j) tmax = max(tmax, tile[j]);
-    kt_need = tmax + 1;
+    kt_need = min(kt_need, tmax + 1);
   }
 
   // ---- operands straight from memory (keys past L and rows past S read 0)
@@ -95,22 +100,24 @@ attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __
     }
   }
 
-  // Masks ride in the S^T accumulator: each product starts from a bias tile
-  // of 0 (visible) or -inf (hidden), so hidden scores come out as -inf with
-  // no per-element work. Register i of lane (g, c) in key tile kt is key
-  // 16kt + 4g + i of row 16t + c. bias[kt] encodes the key length; the
-  // causal diagonal adds key <= row on tile t only.
-  f32x4 bias[NT], diag;
+  // Masks ride in the S^T accumulator: a product starts from 0 (visible) or
+  // -inf (hidden), so hidden scores come out as -inf with no per-element
+  // work. Register i of lane (g, c) in key tile kt is key 16kt + 4g + i of
+  // row 16t + c. Key tiles at or past the key length's tile kL are never
+  // computed except kL itself, which starts from `strad` (keys past L
+  // hidden); the causal diagonal tile starts from `diag` (key <= row).
+  const int kL = L >> 4;  // wave-uniform; L >= 1 below
+  f32x4 strad, diag;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int kt = 0; kt < NT; ++kt) bias[kt][i] = 16 * kt + 4 * g + i < L ? 0.f : -INFINITY;
+    strad[i] = 16 * kL + 4 * g + i < L ? 0.f : -INFINITY;
     diag[i] = 4 * g + i <= c ? 0.f : -INFINITY;
   }
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
   // one query tile, with its index a compile-time constant so that every
-  // register array is indexed statically; every key tile up to the diagonal
-  // (causal) or all of them is computed without branches
+  // register array is indexed statically; the key tiles it sees are
+  // computed without per-element branches
   auto qtile = [&](auto J) {
     constexpr int j = decltype(J)::value;
     const int t = tile[j];
@@ -121,16 +128,22 @@ attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __
       if (LSEp) buf_store4(-INFINITY, rl, g == 0 ? row * 4 : kOutOfRange);
       return;
     }
-    constexpr int NK = (QPW == NT && CAUSAL) ? j + 1 : NT;  // key tiles computed
+    constexpr int NK = (QPW == NT && CAUSAL) ? j + 1 : NT;  // key tiles computed at most
+    // last key tile with a visible key (wave-uniform)
+    const int klast = min(CAUSAL ? t : NT - 1, (L - 1) >> 4);
     f32x4 s[NT];
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < NK; ++kt) {
-      if (CAUSAL && QPW != NT && kt > t) break;  // split waves: tile index is runtime
-      f32x4 init = bias[kt];
+      if (kt > klast) break;
+      f32x4 init = kt == kL ? strad : zero4;
       if (CAUSAL && kt == t) {
+        if (kt == kL) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) init[i] = fminf(init[i], diag[i]);
+          for (int i = 0; i < 4; ++i) init[i] = fminf(init[i], diag[i]);
+        } else {
+          init = diag;
+        }
       }
       s[kt] = mfma_k16(kf[kt], qf[j], init);
       mx = max3(mx, s[kt][0], s[kt][1]);
@@ -140,7 +153,7 @@ attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __
     f32x4 o = {0.f, 0.f, 0.f, 0.f}, lsum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kt = 0; kt < NK; ++kt) {
-      if (CAUSAL && QPW != NT && kt > t) break;
+      if (kt > klast) break;
       T4 pf, pl;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {

@@ -36,6 +36,7 @@ MALL_BYTES = 256 << 20           # working sets below this are rotated over buff
 
 DEFAULT_STEPS = {"tiny": 2000, "launch": 2000, "bandwidth": 100, "compute": 200, "long": 4}
 DEFAULT_WARMUP = {"tiny": 50, "launch": 50, "bandwidth": 5, "compute": 10, "long": 1}
+WARMUP_S = 0.5                   # minimum warm-up time before any timed region
 DEFAULT_GRAPH = {"tiny": 100, "launch": 100, "bandwidth": 0, "compute": 0, "long": 0}
 BOUND = {"tiny": "hbm", "launch": "hbm", "bandwidth": "hbm", "compute": "mfma", "long": "mfma"}
 KERNEL_SOURCES = ("attn_common.h", "attn_mfma.hip", "attn_short.hip", "attn_short16.hip",
@@ -230,9 +231,14 @@ def main():
         mha.forward(qq, kk, vv, causal=w.causal, key_len=kl, out=o, lse=l,
                     variant=args.variant, stream=stream if s is None else s)
 
-    for i in range(W):
+    # untimed warm-up: W steps, and at least WARMUP_S seconds of them, so the
+    # GPU clock has ramped up before the timed region
+    t_w = time.perf_counter()
+    i = 0
+    while i < W or time.perf_counter() - t_w < WARMUP_S:
         step(i)
-    torch.cuda.synchronize()
+        i += 1
+        torch.cuda.synchronize()  # the clock check measures finished work
 
     def timed(run, n):
         """HIP events (on the kernel's stream) and the host wall clock around

@@ -107,12 +107,6 @@ attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __
   // computed except kL itself, which starts from `strad` (keys past L
   // hidden); the causal diagonal tile starts from `diag` (key <= row).
   const int kL = L >> 4;  // wave-uniform; L >= 1 below
-  f32x4 strad, diag;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    strad[i] = 16 * kL + 4 * g + i < L ? 0.f : -INFINITY;
-    diag[i] = 4 * g + i <= c ? 0.f : -INFINITY;
-  }
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
   // one query tile, with its index a compile-time constant so that every
@@ -136,14 +130,11 @@ attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __
 #pragma unroll
     for (int kt = 0; kt < NK; ++kt) {
       if (kt > klast) break;
-      f32x4 init = kt == kL ? strad : zero4;
-      if (CAUSAL && kt == t) {
-        if (kt == kL) {
+      f32x4 init = zero4;
+      if (kt == kL || (CAUSAL && kt == t)) {  // wave-uniform: a tile with hidden keys
+        const int lim = min(L - 1, CAUSAL && kt == t ? row : S) - 16 * kt - 4 * g;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) init[i] = fminf(init[i], diag[i]);
-        } else {
-          init = diag;
-        }
+        for (int i = 0; i < 4; ++i) init[i] = i <= lim ? 0.f : -INFINITY;
       }
       s[kt] = mfma_k16(kf[kt], qf[j], init);
       mx = max3(mx, s[kt][0], s[kt][1]);

@@ -88,21 +88,6 @@ def stored_traffic(workload: str, per_launch_src_hash: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def hold_stream(stream, ms: float) -> None:
-    """Queue about `ms` milliseconds of GPU spin (torch's bounded cycle-count
-    sleep kernel) on `stream`, calibrated once with events."""
-    import torch
-    with torch.cuda.stream(stream):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        cal = 1_000_000
-        a.record(stream)
-        torch.cuda._sleep(cal)
-        b.record(stream)
-        torch.cuda.synchronize()
-        ms_per_cycle = max(a.elapsed_time(b), 1e-3) / cal
-        torch.cuda._sleep(int(min(ms, 500.0) / ms_per_cycle))
-
-
 def cpu_baseline(w, q, k, v, kl, flops_per_pair_unit: int, budget_s: float = 12.0):
     """Time the float64 oracle as it stands on a bounded sample of this workload."""
     import numpy as np
@@ -276,7 +261,7 @@ def main():
         torch.cuda.synchronize()
 
     # ---- timed region: K back-to-back steps (eager, or K / G graph replays)
-    eager_ms, _, wall = timed(eager, K)
+    eager_ms, eager_ev_ms, wall = timed(eager, K)
     ms_per_step = eager_ms
     if graph is not None:
         def replays():
@@ -284,30 +269,17 @@ def main():
                 graph.replay()
         ms_per_step, graph_ev_ms, _ = timed(replays, K)
 
+    # ---- kernel duration: HIP events on the kernel's stream around the timed
+    # region, divided by the launches in it (one launch per step). Launches
+    # run back to back, so this bounds the kernel's own duration from above
+    # by the small gaps between them; an event pair around each single launch
+    # would add its own marker and dispatch overhead instead.
     if graph is not None:
-        # ---- kernel duration, graph replays: the events around the timed
-        # replays divided by the launch count (back-to-back launches; this
-        # bounds the kernel's duration from above, gaps included). An event
-        # pair around one few-microsecond launch would mostly time the pair.
-        k_avg_ms = k_med_ms = graph_ev_ms / K
+        k_avg_ms = graph_ev_ms / K
         kernel_timing = "HIP events around the timed graph replays / %d launches" % K
     else:
-        # ---- kernel duration, eager: a HIP event pair around each launch on
-        # its stream. A bounded GPU spin is queued first so that the host
-        # enqueues every pair before the GPU reaches them.
-        nk = min(K, 200)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(nk)]
-        hold_stream(stream, min(200.0, 3.0 * nk * (wall * 1e3 / K + 0.03)))
-        for i in range(nk):
-            evs[i][0].record(stream)
-            step(i)
-            evs[i][1].record(stream)
-        torch.cuda.synchronize()
-        kms = sorted(a.elapsed_time(b) for a, b in evs)
-        k_avg_ms = sum(kms) / nk
-        k_med_ms = kms[nk // 2]
-        kernel_timing = "HIP event pair around each of %d launches" % nk
+        k_avg_ms = eager_ev_ms / K
+        kernel_timing = "HIP events around the timed region / %d launches" % K
 
     bound = BOUND[w.name]
     if bound == "hbm":
@@ -340,7 +312,7 @@ def main():
         "roofline": {
             "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 5), "traffic": traffic,
-            "kernel_avg_us": round(k_avg_ms * 1e3, 3), "kernel_median_us": round(k_med_ms * 1e3, 3),
+            "kernel_avg_us": round(k_avg_ms * 1e3, 3),
             "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
             "kernel_source_hash": src_hash, "kernel_timing": kernel_timing,
         },

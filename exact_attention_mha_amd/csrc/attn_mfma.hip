@@ -52,8 +52,10 @@ __device__ __forceinline__ int v_key_of_row(int rho) {
   return 16 * (rho >> 4) + 8 * ((rho >> 3) & 1) + 4 * (rho & 1) + ((rho >> 1) & 3);
 }
 
+// Four-wave workgroups ask for two of them per CU (two waves per SIMD), which
+// also keeps matrix-core results in ordinary VGPRs.
 template <typename T, int D, int NQT, int NW, int BK, bool SUM_MFMA, int NST>
-__global__ void __launch_bounds__(NW * 64)
+__global__ void __launch_bounds__(NW * 64, NW == 4 ? 2 : 1)
 attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
               T* __restrict__ Op, float* __restrict__ LSEp, const int32_t* __restrict__ key_len,
               int H, int S, int causal, int n_qblk, float c_log2) {
@@ -370,11 +372,13 @@ static hipError_t launch_general(const AttnParams& p, hipStream_t s) {
   switch (p.D) {
     case 16: return launch_one<T, 16, 2, 4, 64, false>(p, s);
     case 32: return launch_one<T, 32, 2, 4, 64, false>(p, s);
-    case 64:
+    case 64:  // default: 4 waves of 64 query rows, two workgroups per CU
       if (cfg == 1) return launch_one<T, 64, 2, 8, 128, true>(p, s);
       if (cfg == 2) return launch_one<T, 64, 2, 8, 64, true, 3>(p, s);
       if (cfg == 3) return launch_one<T, 64, 2, 8, 64, false>(p, s);
-      return launch_one<T, 64, 2, 8, 64, true>(p, s);
+      if (cfg == 4) return launch_one<T, 64, 2, 8, 64, true>(p, s);
+      if (cfg == 5) return launch_one<T, 64, 2, 4, 64, true>(p, s);
+      return launch_one<T, 64, 4, 4, 64, true>(p, s);
     case 128:
       if (cfg == 1) return launch_one<T, 128, 2, 8, 64, true, 3>(p, s);
       return launch_one<T, 128, 2, 8, 64, true>(p, s);

@@ -9,6 +9,10 @@ Contents:
   attention.py  -- the plain definition, materialising the score matrix
                    (devpost "gpu-transformer-optimization", section 2.1,
                    ops (1)-(5)); full tensors and sampled rows.
+  backward.py   -- the gradients dq, dk, dv of sum(dout * out) by the chain
+                   rule on materialised matrices (rustingstudio
+                   "brain/docs/baseline", "Fused attention", describes the
+                   fused kernels they check).
   gate.py       -- the graded elementwise accuracy rule (devpost
                    "optimized-gpu-kernels-for-transformer-layers",
                    Inspiration; devpost "transformerkernel ... Tesla T4",
@@ -16,6 +20,7 @@ Contents:
 """
 
 from .attention import attention, attention_rows, valid_mask, count_valid_pairs
+from .backward import attention_backward
 from .gate import gate, budget_fraction
 
 __all__ = [
@@ -23,6 +28,7 @@ __all__ = [
     "attention_rows",
     "valid_mask",
     "count_valid_pairs",
+    "attention_backward",
     "gate",
     "budget_fraction",
 ]

@@ -68,6 +68,8 @@ def load() -> ctypes.CDLL:
     lib.mha_forward.restype = ctypes.c_int
     lib.mha_forward_variant.argtypes = args + [ctypes.c_int]
     lib.mha_forward_variant.restype = ctypes.c_int
+    lib.mha_backward.argtypes = [vp] * 10 + [i64, i64, i64, i64, ctypes.c_int, vp, ctypes.c_int, vp]
+    lib.mha_backward.restype = ctypes.c_int
     lib.mha_select_variant.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
     lib.mha_select_variant.restype = ctypes.c_int
     lib.mha_variant_name.argtypes = [ctypes.c_int]
@@ -154,3 +156,56 @@ def forward(q, k, v, causal: bool = False, key_len=None, out=None, lse=None,
     if status != 0:
         raise MhaError("mha_forward", status, lib.mha_status_string(status).decode())
     return out, lse
+
+
+def backward(q, k, v, out, lse, dout, causal: bool = False, key_len=None,
+             dq=None, dk=None, dv=None, delta=None, stream=None):
+    """Gradients (dq, dk, dv) of sum(dout * out) through the attention forward.
+
+    Args:
+      q, k, v, causal, key_len: exactly as passed to forward().
+      out, lse: forward()'s outputs for those inputs (lse is required).
+      dout: the output gradient, contiguous [B, H, S, d_h], dtype of q.
+      dq, dk, dv: optional preallocated outputs shaped and typed like q.
+      delta: optional float32 [B, H, S] workspace; receives rowsum(dout * out).
+      stream: a torch.cuda.Stream (default: the current stream).
+    Returns:
+      (dq, dk, dv).
+    """
+    import torch
+
+    lib = load()
+    B, H, S, D = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor shaped and typed like q")
+    if (lse is None or lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_cuda
+            or not lse.is_contiguous()):
+        raise ValueError("lse must be forward()'s contiguous float32 GPU tensor [B, H, S]")
+    dcode = _dtype_code(q)
+    grads = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            t = torch.empty_like(q)
+        elif t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor shaped and typed like q")
+        grads.append(t)
+    if delta is None:
+        delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    elif (delta.shape != (B, H, S) or delta.dtype != torch.float32 or not delta.is_cuda
+          or not delta.is_contiguous()):
+        raise ValueError("delta must be a contiguous float32 GPU tensor [B, H, S]")
+    kl_ptr = None
+    if key_len is not None:
+        if (key_len.dtype != torch.int32 or key_len.shape != (B,) or not key_len.is_cuda
+                or not key_len.is_contiguous()):
+            raise ValueError("key_len must be a contiguous int32 GPU tensor [B]")
+        kl_ptr = key_len.data_ptr()
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    status = lib.mha_backward(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+        lse.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
+        delta.data_ptr(), B, H, S, D, int(bool(causal)), kl_ptr, dcode, st.cuda_stream)
+    if status != 0:
+        raise MhaError("mha_backward", status, lib.mha_status_string(status).decode())
+    return tuple(grads)

@@ -1,0 +1,579 @@
+// Attention backward on the gfx950 matrix cores (fp16 / bf16 inputs, fp32
+// accumulation): dQ, dK, dV of sum(dO * O) for O = softmax(Q K^T / sqrt(d_h)
+// + mask) V.
+//
+// Two kernels, as in the fused backward of rustingstudio "brain/docs/baseline"
+// ("Fused attention"): the query gradient is complete inside a query tile and
+// the key / value gradients inside a key tile, so
+//   * attn_bwd_dq   walks key blocks for a block of query rows, and
+//   * attn_bwd_dkv  walks query blocks for a block of key rows,
+// and both rebuild the probabilities from the stored log-sum-exp instead of
+// keeping them: P = exp(S / sqrt(d_h) - lse). With dP = dO V^T and the row
+// term D = rowsum(dO * O) (equal to rowsum(P * dP) since O = P V),
+//   dS = P * (dP - D),  dQ = dS K / sqrt(d_h),  dK = dS^T Q / sqrt(d_h),
+//   dV = P^T dO.
+// D goes through the caller's workspace: for fp16 the dq kernel computes it
+// from dO and the forward's output and writes it; for bf16 a first pass of
+// the dq kernel accumulates rowsum(P * dP) exactly and writes it, and the dq
+// pass proper reads it. The dkv kernel, launched after them on the same
+// stream, reads it.
+//
+// Products are formed transposed where that puts the contraction index in
+// the operand registers directly (lane = 16g + c):
+//   dq : S^T = K Q^T, dP^T = V dO^T (A operand: K / V rows from LDS,
+//        B operand: Q / dO fragments in registers), dQ^T += K^T dS^T
+//        (A operand: K read transposed from LDS, B operand: dS^T as the
+//        S^T result tiles leave it).
+//   dkv: S = Q K^T, dP = dO V^T (A: Q / dO rows from LDS, B: K / V fragments
+//        in registers), dV^T += dO^T P and dK^T += Q^T dS (A: dO / Q read
+//        transposed from LDS, B: P / dS as the result tiles leave them).
+// P and dS are rounded to the input dtype as matrix-core operands; for bf16
+// each is split into a bf16 head and a bf16 remainder (two products), since
+// a single bf16 rounding of P or dS is too coarse for the accuracy rule.
+//
+// A 32-row pair of an LDS operand block is read both as 16-row tiles (one
+// 128-bit row read per lane) and transposed (ds_read_b64_tr_b16 over 4 rows
+// per lane group). Row c of tile h of the pair is stored at LDS row
+// 16h + 2(c % 8) + c / 8 of the pair: a tile read then covers 16 distinct
+// padded rows, and each half-wave of a transposed read 8 rows of one parity,
+// which keeps both kinds of read free of bank conflicts. In the contraction
+// over a pair, k-slot 8g + 4h + i of lane group g stands for row 16h + 4g + i
+// of the pair, in both operands.
+#include "attn_common.h"
+#include "launch.h"
+
+namespace mha {
+
+// LDS row (within a 32-row pair) of pair row x, and the pair row stored at
+// LDS row r.
+__device__ __forceinline__ int bwd_lds_row(int x) {
+  const int c = x & 15;
+  return (x & 16) + 2 * (c & 7) + (c >> 3);
+}
+__device__ __forceinline__ int bwd_row_at(int r) {
+  const int cc = r & 15;
+  return (r & 16) + 8 * (cc & 1) + (cc >> 1);
+}
+
+// Per-lane DMA slots of an operand block of NR rows x D columns in the
+// padded pair-permuted LDS layout: fills the source byte offsets (relative
+// to the block's first row; kOutOfRange for pad slots) of this wave's slots.
+template <typename T, int D, int NR, int NW>
+struct BwdTile {
+  static constexpr int STR = D + 8;
+  static constexpr int SPR = D / 8 + 1;
+  static constexpr int SLOTS = NR * SPR;
+  static constexpr int NI = (SLOTS + 63) / 64;
+  static constexpr int ELEMS = NI * 64 * 8;  // whole DMA instructions
+  static constexpr int NIW = (NI + NW - 1) / NW;
+  static constexpr int RB = D * (int)sizeof(T);
+  __device__ static void offsets(int wave, int lane, int (&off)[NIW]) {
+#pragma unroll
+    for (int i = 0; i < NIW; ++i) {
+      const int slot = (wave + i * NW) * 64 + lane;
+      const int row = slot / SPR, j = slot - row * SPR;
+      const bool live = slot < SLOTS && j < D / 8;
+      off[i] = live ? (32 * (row >> 5) + bwd_row_at(row & 31)) * RB + 16 * j : kOutOfRange;
+    }
+  }
+  __device__ static void copy(rsrc_t r, T* dst, const int (&off)[NIW], int wave, int soff) {
+#pragma unroll
+    for (int i = 0; i < NIW; ++i) {
+      const int inst = wave + i * NW;
+      if (NI % NW == 0 || inst < NI) dma16(r, dst + inst * 512, off[i], soff);
+    }
+  }
+};
+
+// ---------------------------------------------------------------- dq kernel
+// MODE kRowFromOut: D = rowsum(dO * O) from the forward's output, written to
+//   the workspace, then dQ (fp16: the output's rounding leaves D well inside
+//   the accuracy rule).
+// MODE kRowPass: no dQ; D = rowsum(P * dP) accumulated over every visible key
+//   in fp32 and written to the workspace (bf16: the output rounded to bf16
+//   puts an error of D times sum_j P_ij k_j into dQ, which rows with few
+//   visible keys do not average away).
+// MODE kRowRead: dQ with D read from the workspace.
+constexpr int kRowFromOut = 0, kRowPass = 1, kRowRead = 2;
+
+template <typename T, int D, int NQT, int NW, int BK, int MODE>
+__global__ void __launch_bounds__(NW * 64, 2)
+attn_bwd_dq(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
+            const T* __restrict__ Op, const T* __restrict__ dOp, const float* __restrict__ LSEp,
+            T* __restrict__ dQp, float* __restrict__ Dp, const int32_t* __restrict__ key_len,
+            int H, int S, int causal, int n_qblk, float c_log2, float scale) {
+  typedef typename Vec<T>::x8 T8;
+  typedef typename Vec<T>::x4 T4;
+  typedef BwdTile<T, D, BK, NW> Tile;
+  constexpr int STR = Tile::STR;
+  constexpr int NDT = D / 16;
+  constexpr int NKT = BK / 16;
+  constexpr int NKP = BK / 32;
+  constexpr int NKC = D >= 32 ? D / 32 : 1;
+  constexpr int RB = D * (int)sizeof(T);
+  constexpr int BQ = NW * NQT * 16;
+  constexpr bool kBf16 = __is_same(T, bf16_t);
+  static_assert(BK % 32 == 0 && D % 16 == 0, "tile shape");
+
+  __shared__ __attribute__((aligned(16))) T smem[2 * 2 * Tile::ELEMS];  // [stage][K, V]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+
+  const uint32_t logical = xcd_logical_id(blockIdx.x, gridDim.x);
+  const uint32_t bh = logical / (uint32_t)n_qblk;
+  int qb = (int)(logical - bh * (uint32_t)n_qblk);
+  if (causal) qb = n_qblk - 1 - qb;  // heaviest causal tiles first
+  const int b = (int)(bh / (uint32_t)H);
+  const int L = clamp_len(key_len, b, S);
+  const int64_t head = (int64_t)bh * S * D;
+  const int q_start = qb * BQ;
+  const int q_end = min(S, q_start + BQ);
+  const int kend = causal ? min(L, q_end) : L;
+  const int nblk = (kend + BK - 1) / BK;
+  const int wq0 = q_start + wave * NQT * 16;
+  const bool wave_live = wq0 < S;
+  const int kend_w = !wave_live ? 0 : (causal ? min(L, min(q_end, wq0 + NQT * 16)) : L);
+
+  const rsrc_t rq = make_rsrc(Qp + head, (uint32_t)S * RB);
+  const rsrc_t ro = make_rsrc(Op + head, (uint32_t)S * RB);
+  const rsrc_t rdo = make_rsrc(dOp + head, (uint32_t)S * RB);
+  const rsrc_t rdq = make_rsrc(dQp + head, (uint32_t)S * RB);
+  const rsrc_t rl = make_rsrc(LSEp + (int64_t)bh * S, (uint32_t)S * 4);
+  const rsrc_t rd = make_rsrc(Dp + (int64_t)bh * S, (uint32_t)S * 4);
+
+  // ---- Q and dO fragments (B operands, query column c), and the row term
+  //      D = rowsum(dO * O) of each of this wave's rows
+  T8 qf[NQT][NKC], dof[NQT][NKC];
+  T4 qf4[NQT], dof4[NQT];
+  float drow[NQT], nlse2[NQT];
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    const int row = wq0 + 16 * t + c;
+    float acc = 0.f;
+    if constexpr (D == 16) {
+      qf4[t] = buf_load8<T4>(rq, (row * D + 4 * g) * 2, 0);
+      dof4[t] = buf_load8<T4>(rdo, (row * D + 4 * g) * 2, 0);
+      if constexpr (MODE == kRowFromOut) {
+        const T4 of = buf_load8<T4>(ro, (row * D + 4 * g) * 2, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc += to_f(dof4[t][e]) * to_f(of[e]);
+      }
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        qf[t][kc] = buf_load16<T8>(rq, (row * D + 32 * kc + 8 * g) * 2, 0);
+        dof[t][kc] = buf_load16<T8>(rdo, (row * D + 32 * kc + 8 * g) * 2, 0);
+        if constexpr (MODE == kRowFromOut) {
+          const T8 of = buf_load16<T8>(ro, (row * D + 32 * kc + 8 * g) * 2, 0);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc += to_f(dof[t][kc][e]) * to_f(of[e]);
+        }
+      }
+    }
+    if constexpr (MODE == kRowFromOut) {
+      drow[t] = group_sum(acc);
+      if (wave_live) buf_store4(drow[t], rd, g == 0 ? row * 4 : kOutOfRange);
+    } else if constexpr (MODE == kRowRead) {
+      drow[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, row * 4, 0, 0));
+    } else {
+      drow[t] = 0.f;  // accumulates rowsum(P * dP) of this lane's keys
+    }
+    const float lse = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, row * 4, 0, 0));
+    nlse2[t] = -lse * kLog2e;
+  }
+  wait_vmem();
+
+  f32x4 acc_dq[NQT][NDT];
+#pragma unroll
+  for (int t = 0; t < NQT; ++t)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc_dq[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (nblk > 0) {
+    const rsrc_t rk = make_rsrc(Kp + head, (uint32_t)kend * RB);
+    const rsrc_t rv = make_rsrc(Vp + head, (uint32_t)kend * RB);
+    int off[Tile::NIW];
+    Tile::offsets(wave, lane, off);
+    auto dma_block = [&](int st, int k0) {
+      T* Kst = smem + st * 2 * Tile::ELEMS;
+      Tile::copy(rk, Kst, off, wave, k0 * RB);
+      Tile::copy(rv, Kst + Tile::ELEMS, off, wave, k0 * RB);
+    };
+    dma_block(0, 0);
+
+    // per-lane LDS offsets (elements): tile row c of a pair (row reads), and
+    // the transposed read of lane group g (rows 4g + c/4, column 4(c%4))
+    const int rrow = bwd_lds_row(c) * STR;
+    const int trow = bwd_lds_row(4 * g + (c >> 2)) * STR + 4 * (c & 3);
+
+    for (int kb = 0; kb < nblk; ++kb) {
+      const int k0 = kb * BK;
+      wait_vmem();
+      block_barrier();
+      if (kb + 1 < nblk) dma_block((kb + 1) & 1, k0 + BK);
+      if (k0 >= kend_w) continue;  // wave-uniform
+
+      const T* Ks = smem + (kb & 1) * 2 * Tile::ELEMS;
+      const T* Vs = Ks + Tile::ELEMS;
+
+      // S^T = K Q^T and dP^T = V dO^T; key 16kt + 4g + i of the block in
+      // register i of lane (g, c)
+      f32x4 s[NQT][NKT], dp[NQT][NKT];
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+        const int rb = 16 * kt * STR + rrow;
+#pragma unroll
+        for (int t = 0; t < NQT; ++t) s[t][kt] = dp[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (D == 16) {
+          const T4 kf = *(const T4*)(Ks + rb + 4 * g);
+          const T4 vf = *(const T4*)(Vs + rb + 4 * g);
+#pragma unroll
+          for (int t = 0; t < NQT; ++t) {
+            s[t][kt] = mfma_k16(kf, qf4[t], s[t][kt]);
+            dp[t][kt] = mfma_k16(vf, dof4[t], dp[t][kt]);
+          }
+        } else {
+#pragma unroll
+          for (int kc = 0; kc < NKC; ++kc) {
+            const T8 kf = *(const T8*)(Ks + rb + 32 * kc + 8 * g);
+            const T8 vf = *(const T8*)(Vs + rb + 32 * kc + 8 * g);
+#pragma unroll
+            for (int t = 0; t < NQT; ++t) {
+              s[t][kt] = mfma_k32(kf, qf[t][kc], s[t][kt]);
+              dp[t][kt] = mfma_k32(vf, dof[t][kc], dp[t][kt]);
+            }
+          }
+        }
+      }
+
+      // P = exp(S / sqrt(d) - lse) (0 for hidden pairs), dS = P (dP - D)
+      const bool edge = (k0 + BK > L) || (causal && (k0 + BK - 1 > wq0));
+      T8 dsf[NQT][NKP], dsl[NQT][NKP];
+#pragma unroll
+      for (int t = 0; t < NQT; ++t) {
+        const int row = wq0 + 16 * t + c;
+        const int lim = (causal ? min(L - 1, row) : L - 1) - k0 - 4 * g;  // max visible key offset
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float p = fast_exp2(fmaf(s[t][kt][i], c_log2, nlse2[t]));
+            if (edge && 16 * kt + i > lim) p = 0.f;
+            if constexpr (MODE == kRowPass) {
+              drow[t] = fmaf(p, dp[t][kt][i], drow[t]);
+              continue;
+            }
+            const float d = p * (dp[t][kt][i] - drow[t]);
+            const T dh = to_t<T>(d);
+            dsf[t][kt >> 1][4 * (kt & 1) + i] = dh;
+            if constexpr (kBf16) dsl[t][kt >> 1][4 * (kt & 1) + i] = to_t<T>(d - to_f(dh));
+          }
+      }
+
+      // dQ^T += K^T dS^T, one key pair at a time
+      if constexpr (MODE == kRowPass) continue;
+#pragma unroll
+      for (int p = 0; p < NKP; ++p) {
+        const T* kt0 = Ks + 32 * p * STR + trow;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const i16x4 a0 = lds_read_tr16(kt0 + 16 * dt);
+          const i16x4 a1 = lds_read_tr16(kt0 + 16 * STR + 16 * dt);
+          const T8 kf = __builtin_bit_cast(T8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int t = 0; t < NQT; ++t) {
+            acc_dq[t][dt] = mfma_k32(kf, dsf[t][p], acc_dq[t][dt]);
+            if constexpr (kBf16) acc_dq[t][dt] = mfma_k32(kf, dsl[t][p], acc_dq[t][dt]);
+          }
+        }
+      }
+    }
+  }
+
+  if constexpr (MODE == kRowPass) {
+#pragma unroll
+    for (int t = 0; t < NQT; ++t) {
+      const float dsum = group_sum(drow[t]);
+      if (wave_live) buf_store4(dsum, rd, g == 0 ? (wq0 + 16 * t + c) * 4 : kOutOfRange);
+    }
+    return;
+  }
+
+  // ---- dQ = dQ^T^T / sqrt(d): row c, columns 16dt + 4g .. 16dt + 4g + 3
+  if (wave_live) {
+#pragma unroll
+    for (int t = 0; t < NQT; ++t) {
+      const int row = wq0 + 16 * t + c;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        T4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = to_t<T>(acc_dq[t][dt][i] * scale);
+        buf_store8(v, rdq, (row * D + 16 * dt + 4 * g) * 2);
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------- dkv kernel
+template <typename T, int D, int NKTW, int NW, int BQb>
+__global__ void __launch_bounds__(NW * 64, 2)
+attn_bwd_dkv(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
+             const T* __restrict__ dOp, const float* __restrict__ LSEp, const float* __restrict__ Dp,
+             T* __restrict__ dKp, T* __restrict__ dVp, const int32_t* __restrict__ key_len,
+             int H, int S, int causal, int n_kblk, float c_log2, float scale) {
+  typedef typename Vec<T>::x8 T8;
+  typedef typename Vec<T>::x4 T4;
+  typedef BwdTile<T, D, BQb, NW> Tile;
+  constexpr int STR = Tile::STR;
+  constexpr int NDT = D / 16;
+  constexpr int NQP = BQb / 32;  // query pairs per block
+  constexpr int NKC = D >= 32 ? D / 32 : 1;
+  constexpr int RB = D * (int)sizeof(T);
+  constexpr int BKW = NW * NKTW * 16;  // keys per workgroup
+  constexpr bool kBf16 = __is_same(T, bf16_t);
+  constexpr int ROWF = 64;             // floats in one row-vector stage (one DMA instruction)
+  static_assert(BQb % 32 == 0 && BQb <= ROWF && D % 16 == 0, "tile shape");
+
+  // [stage][Q, dO][lse, D]
+  __shared__ __attribute__((aligned(16))) T smem[2 * 2 * Tile::ELEMS];
+  __shared__ __attribute__((aligned(16))) float svec[2 * 2 * ROWF];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+
+  const uint32_t logical = xcd_logical_id(blockIdx.x, gridDim.x);
+  const uint32_t bh = logical / (uint32_t)n_kblk;
+  const int kb = (int)(logical - bh * (uint32_t)n_kblk);
+  const int b = (int)(bh / (uint32_t)H);
+  const int L = clamp_len(key_len, b, S);
+  const int64_t head = (int64_t)bh * S * D;
+  const int k_start = kb * BKW;
+  const int wk0 = k_start + wave * NKTW * 16;
+  const rsrc_t rdk = make_rsrc(dKp + head, (uint32_t)S * RB);
+  const rsrc_t rdv = make_rsrc(dVp + head, (uint32_t)S * RB);
+
+  // queries that see any key of the workgroup: all when not causal, else
+  // from its first visible key on; none past the key length
+  const int q_lo = causal ? min(k_start, L) / BQb * BQb : 0;
+  const int nblk = k_start >= L ? 0 : (S - q_lo + BQb - 1) / BQb;
+
+  // ---- K and V fragments (B operands, key column c) for this wave's tiles
+  const rsrc_t rk = make_rsrc(Kp + head, (uint32_t)L * RB);
+  const rsrc_t rv = make_rsrc(Vp + head, (uint32_t)L * RB);
+  T8 kf[NKTW][NKC], vf[NKTW][NKC];
+  T4 kf4[NKTW], vf4[NKTW];
+#pragma unroll
+  for (int t = 0; t < NKTW; ++t) {
+    const int key = wk0 + 16 * t + c;
+    if constexpr (D == 16) {
+      kf4[t] = buf_load8<T4>(rk, (key * D + 4 * g) * 2, 0);
+      vf4[t] = buf_load8<T4>(rv, (key * D + 4 * g) * 2, 0);
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        kf[t][kc] = buf_load16<T8>(rk, (key * D + 32 * kc + 8 * g) * 2, 0);
+        vf[t][kc] = buf_load16<T8>(rv, (key * D + 32 * kc + 8 * g) * 2, 0);
+      }
+    }
+  }
+  wait_vmem();
+
+  f32x4 adk[NKTW][NDT], adv[NKTW][NDT];
+#pragma unroll
+  for (int t = 0; t < NKTW; ++t)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) adk[t][dt] = adv[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (nblk > 0) {
+    const rsrc_t rq = make_rsrc(Qp + head, (uint32_t)S * RB);
+    const rsrc_t rdo = make_rsrc(dOp + head, (uint32_t)S * RB);
+    const rsrc_t rl = make_rsrc(LSEp + (int64_t)bh * S, (uint32_t)S * 4);
+    const rsrc_t rd = make_rsrc(Dp + (int64_t)bh * S, (uint32_t)S * 4);
+    int off[Tile::NIW];
+    Tile::offsets(wave, lane, off);
+    // row vectors (lse, D of the block's rows): lane i of wave 0 copies one
+    // float of each; lanes past the block (and rows past S) write zeros
+    const int voff = lane < BQb ? 4 * lane : kOutOfRange;
+    auto dma_block = [&](int st, int q0) {
+      T* Qst = smem + st * 2 * Tile::ELEMS;
+      Tile::copy(rq, Qst, off, wave, q0 * RB);
+      Tile::copy(rdo, Qst + Tile::ELEMS, off, wave, q0 * RB);
+      if (wave == 0) {
+        dma4(rl, svec + st * 2 * ROWF, voff, q0 * 4);
+        dma4(rd, svec + st * 2 * ROWF + ROWF, voff, q0 * 4);
+      }
+    };
+    dma_block(0, q_lo);
+
+    const int rrow = bwd_lds_row(c) * STR;
+    const int trow = bwd_lds_row(4 * g + (c >> 2)) * STR + 4 * (c & 3);
+
+    for (int qb = 0; qb < nblk; ++qb) {
+      const int q0 = q_lo + qb * BQb;
+      wait_vmem();
+      block_barrier();
+      if (qb + 1 < nblk) dma_block((qb + 1) & 1, q0 + BQb);
+
+      const T* Qs = smem + (qb & 1) * 2 * Tile::ELEMS;
+      const T* dOs = Qs + Tile::ELEMS;
+      const float* ls = svec + (qb & 1) * 2 * ROWF;
+      const float* ds = ls + ROWF;
+      // a block needs masking if it reaches past S, or (causal) has a
+      // query before some key of this wave
+      const bool edge = (q0 + BQb > S) || (causal && q0 < wk0 + NKTW * 16 - 1) || (wk0 + NKTW * 16 > L);
+
+#pragma unroll
+      for (int p = 0; p < NQP; ++p) {
+        // S = Q K^T and dP = dO V^T for the pair's two query tiles h:
+        // register i of lane (g, c) is query 32p + 16h + 4g + i, key column c
+        f32x4 s[2][NKTW], dp[2][NKTW];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int rb = (32 * p + 16 * h) * STR + rrow;
+#pragma unroll
+          for (int t = 0; t < NKTW; ++t) s[h][t] = dp[h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if constexpr (D == 16) {
+            const T4 qa = *(const T4*)(Qs + rb + 4 * g);
+            const T4 da = *(const T4*)(dOs + rb + 4 * g);
+#pragma unroll
+            for (int t = 0; t < NKTW; ++t) {
+              s[h][t] = mfma_k16(qa, kf4[t], s[h][t]);
+              dp[h][t] = mfma_k16(da, vf4[t], dp[h][t]);
+            }
+          } else {
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) {
+              const T8 qa = *(const T8*)(Qs + rb + 32 * kc + 8 * g);
+              const T8 da = *(const T8*)(dOs + rb + 32 * kc + 8 * g);
+#pragma unroll
+              for (int t = 0; t < NKTW; ++t) {
+                s[h][t] = mfma_k32(qa, kf[t][kc], s[h][t]);
+                dp[h][t] = mfma_k32(da, vf[t][kc], dp[h][t]);
+              }
+            }
+          }
+        }
+        // P and dS as B operands: k-slot 8g + 4h + i is query 32p + 16h + 4g + i
+        T8 pf[NKTW], dsf[NKTW], pl[NKTW], dsl[NKTW];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int qr = 32 * p + 16 * h + 4 * g;  // block row of register 0
+          const f32x4 lv = *(const f32x4*)(ls + qr);
+          const f32x4 dv = *(const f32x4*)(ds + qr);
+#pragma unroll
+          for (int t = 0; t < NKTW; ++t) {
+            const int key = wk0 + 16 * t + c;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float pr = fast_exp2(fmaf(s[h][t][i], c_log2, -lv[i] * kLog2e));
+              if (edge) {
+                const int q = q0 + qr + i;
+                if (q >= S || key >= L || (causal && key > q)) pr = 0.f;
+              }
+              const float d = pr * (dp[h][t][i] - dv[i]);
+              const T ph = to_t<T>(pr), dh = to_t<T>(d);
+              pf[t][4 * h + i] = ph;
+              dsf[t][4 * h + i] = dh;
+              if constexpr (kBf16) {
+                pl[t][4 * h + i] = to_t<T>(pr - to_f(ph));
+                dsl[t][4 * h + i] = to_t<T>(d - to_f(dh));
+              }
+            }
+          }
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS over the pair's 32 queries
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int tb = 32 * p * STR + trow + 16 * dt;
+          const i16x4 o0 = lds_read_tr16(dOs + tb);
+          const i16x4 o1 = lds_read_tr16(dOs + tb + 16 * STR);
+          const i16x4 q0r = lds_read_tr16(Qs + tb);
+          const i16x4 q1r = lds_read_tr16(Qs + tb + 16 * STR);
+          const T8 oa = __builtin_bit_cast(T8, __builtin_shufflevector(o0, o1, 0, 1, 2, 3, 4, 5, 6, 7));
+          const T8 qa = __builtin_bit_cast(T8, __builtin_shufflevector(q0r, q1r, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int t = 0; t < NKTW; ++t) {
+            adv[t][dt] = mfma_k32(oa, pf[t], adv[t][dt]);
+            adk[t][dt] = mfma_k32(qa, dsf[t], adk[t][dt]);
+            if constexpr (kBf16) {
+              adv[t][dt] = mfma_k32(oa, pl[t], adv[t][dt]);
+              adk[t][dt] = mfma_k32(qa, dsl[t], adk[t][dt]);
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // ---- dK = (dK^T)^T / sqrt(d), dV = (dV^T)^T: key row c, columns
+  //      16dt + 4g .. 16dt + 4g + 3 (zero for keys past the key length)
+#pragma unroll
+  for (int t = 0; t < NKTW; ++t) {
+    const int key = wk0 + 16 * t + c;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      T4 vk, vv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vk[i] = to_t<T>(adk[t][dt][i] * scale);
+        vv[i] = to_t<T>(adv[t][dt][i]);
+      }
+      buf_store8(vk, rdk, (key * D + 16 * dt + 4 * g) * 2);
+      buf_store8(vv, rdv, (key * D + 16 * dt + 4 * g) * 2);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+template <typename T, int D, int NQT, int NW, int BK, int NKTW, int BQb>
+static hipError_t launch_bwd_one(const BwdParams& p, hipStream_t s) {
+  constexpr int BQ = NW * NQT * 16;
+  constexpr int BKW = NW * NKTW * 16;
+  const int n_qblk = (p.S + BQ - 1) / BQ;
+  const int n_kblk = (p.S + BKW - 1) / BKW;
+  const int64_t wq = (int64_t)p.B * p.H * n_qblk, wk = (int64_t)p.B * p.H * n_kblk;
+  if (wq > 0x7fffffffLL || wk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const float scale = 1.f / sqrtf((float)p.D);
+  constexpr bool kBf16 = __is_same(T, bf16_t);
+  if constexpr (kBf16) {
+    hipLaunchKernelGGL((attn_bwd_dq<T, D, NQT, NW, BK, kRowPass>), dim3((unsigned)wq), dim3(NW * 64), 0, s,
+                       (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.out, (const T*)p.dout,
+                       p.lse, (T*)p.dq, p.delta, p.key_len, p.H, p.S, p.causal, n_qblk, p.c_log2, scale);
+    hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+  }
+  constexpr int kDqMode = kBf16 ? kRowRead : kRowFromOut;
+  hipLaunchKernelGGL((attn_bwd_dq<T, D, NQT, NW, BK, kDqMode>), dim3((unsigned)wq), dim3(NW * 64), 0, s,
+                     (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.out, (const T*)p.dout,
+                     p.lse, (T*)p.dq, p.delta, p.key_len, p.H, p.S, p.causal, n_qblk, p.c_log2, scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bwd_dkv<T, D, NKTW, NW, BQb>), dim3((unsigned)wk), dim3(NW * 64), 0, s,
+                     (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.dout, p.lse, p.delta,
+                     (T*)p.dk, (T*)p.dv, p.key_len, p.H, p.S, p.causal, n_kblk, p.c_log2, scale);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
+  switch (p.D) {
+    case 16: return launch_bwd_one<T, 16, 2, 4, 64, 2, 64>(p, s);
+    case 32: return launch_bwd_one<T, 32, 2, 4, 64, 2, 64>(p, s);
+    case 64: return launch_bwd_one<T, 64, 2, 4, 64, 2, 64>(p, s);
+    case 128: return launch_bwd_one<T, 128, 1, 4, 64, 1, 64>(p, s);
+    case 256: return launch_bwd_one<T, 256, 1, 4, 32, 1, 32>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
+  if (p.dtype == 1) return launch_bwd_t<f16_t>(p, s);
+  if (p.dtype == 2) return launch_bwd_t<bf16_t>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mha

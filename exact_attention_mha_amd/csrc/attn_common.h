@@ -144,6 +144,11 @@ __device__ __forceinline__ void dma16(rsrc_t r, void* lds, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
                                            voff, soff, 0, 0);
 }
+// The same with 4 bytes per lane: lane i's 4 bytes land at lds + 4*i.
+__device__ __forceinline__ void dma4(rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4,
+                                           voff, soff, 0, 0);
+}
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left unconstrained)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 // s_waitcnt vmcnt(N): at most N (the most recent) vector-memory operations

@@ -24,6 +24,28 @@ struct AttnParams {
   int tile_cfg;            // tile-shape table entry (0 = default)
 };
 
+// Backward: dq, dk, dv of sum(dout * out); delta is the caller's float
+// [B, H, S] workspace for the row term rowsum(dout * out).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;
+  const int32_t* key_len;  // nullable
+  int B, H, S, D;
+  int causal;
+  int dtype;
+  float c_log2;
+};
+
+hipError_t launch_bwd(const BwdParams& p, hipStream_t s);          // dq then dk/dv kernel
+
 hipError_t launch_mfma(const AttnParams& p, hipStream_t s);        // general tiled
 hipError_t launch_mfma_small(const AttnParams& p, hipStream_t s);  // few rows per WG
 hipError_t launch_f32(const AttnParams& p, hipStream_t s);         // fp32 inputs

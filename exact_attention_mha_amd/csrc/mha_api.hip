@@ -120,6 +120,43 @@ int mha_forward(const void* q, const void* k, const void* v, void* out, float* l
                              MHA_VARIANT_AUTO);
 }
 
+int mha_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t B,
+                 int64_t H, int64_t S, int64_t d_h, int causal, const int32_t* key_len, int dtype,
+                 void* stream) {
+  int st = validate(q, k, v, dq, lse, B, H, S, d_h, key_len, dtype);
+  if (st != MHA_OK) return st;
+  if (dtype == MHA_F32) return MHA_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0 || S == 0) return MHA_OK;
+  if (!out || !dout || !lse || !dk || !dv || !delta) return MHA_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(dout, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(delta, 4))
+    return MHA_ERR_MISALIGNED;
+
+  mha::BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.delta = delta;
+  p.key_len = key_len;
+  p.B = (int)B;
+  p.H = (int)H;
+  p.S = (int)S;
+  p.D = (int)d_h;
+  p.causal = causal ? 1 : 0;
+  p.dtype = dtype;
+  p.c_log2 = (float)(1.4426950408889634074 / sqrt((double)d_h));
+  const hipError_t e = mha::launch_bwd(p, (hipStream_t)stream);
+  if (e == hipErrorInvalidConfiguration) return MHA_ERR_SHAPE;
+  return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
+}
+
 int mha_select_variant(int64_t B, int64_t H, int64_t S, int64_t d_h, int causal, int dtype) {
   (void)causal;
   if (B < 0 || H < 0 || S < 0 || d_h <= 0) return -MHA_ERR_SHAPE;
@@ -152,6 +189,6 @@ const char* mha_status_string(int status) {
   return "unknown status";
 }
 
-int mha_version(void) { return 100; }
+int mha_version(void) { return 101; }
 
 }  // extern "C"

@@ -105,6 +105,39 @@ int mha_forward_variant(const void* q, const void* k, const void* v, void* out, 
                         int64_t B, int64_t H, int64_t S, int64_t d_h, int causal,
                         const int32_t* key_len, int dtype, void* stream, int variant);
 
+/*
+ * mha_backward -- enqueue the gradients of the forward above on `stream`.
+ *
+ * Given the output gradient dout of a loss, writes dq, dk, dv: the
+ * gradients of sum(dout * out) with respect to q, k and v, for the same
+ * mask. Two kernels, as in the fused backward of rustingstudio
+ * "brain/docs/baseline" ("Fused attention"): one per block of query rows
+ * (dq), one per block of key rows (dk, dv); both rebuild the probabilities
+ * from the forward's log-sum-exp, P = exp(q.k / sqrt(d_h) - lse), and take
+ * the softmax row term from dout and out: D = rowsum(dout * out).
+ *
+ *   q, k, v      the forward's inputs (as for mha_forward). Read only.
+ *   out, lse     the forward's outputs for exactly these inputs and mask
+ *                (lse is required here). Read only.
+ *   dout         device pointer, [B, H, S, d_h] of `dtype`. Read only.
+ *   dq, dk, dv   device pointers, [B, H, S, d_h] of `dtype`, 16-byte
+ *                aligned; written in full (dk = dv = 0 for keys past the
+ *                key length). Must not overlap any input.
+ *   delta        caller-owned float workspace [B, H, S], 4-byte aligned;
+ *                overwritten with D (it stays valid after the call).
+ *   B .. dtype   as for mha_forward; dtype must be MHA_F16 or MHA_BF16
+ *                (fp32 inputs return MHA_ERR_UNSUPPORTED).
+ *
+ * Precision: products on the matrix cores with fp32 accumulation; the
+ * probabilities and dS are rounded to the input dtype as matrix-core
+ * operands; outputs rounded once to the input dtype.
+ * Ownership, asynchrony and error behaviour as for mha_forward.
+ */
+int mha_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t B,
+                 int64_t H, int64_t S, int64_t d_h, int causal, const int32_t* key_len, int dtype,
+                 void* stream);
+
 /* The variant mha_forward would launch for these arguments (host-only, no
  * GPU call), or a negative mha_status code if the arguments are invalid. */
 int mha_select_variant(int64_t B, int64_t H, int64_t S, int64_t d_h, int causal, int dtype);
@@ -115,7 +148,7 @@ const char* mha_variant_name(int variant);
 /* Static description of a status code. */
 const char* mha_status_string(int status);
 
-/* Library ABI version (major * 100 + minor). */
+/* Library ABI version (major * 100 + minor); 101 adds mha_backward. */
 int mha_version(void);
 
 #ifdef __cplusplus

@@ -20,7 +20,7 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for want in ("mha_forward", "mha_forward_variant", "mha_select_variant",
+    for want in ("mha_forward", "mha_forward_variant", "mha_backward", "mha_select_variant",
                  "mha_status_string", "mha_variant_name", "mha_version"):
         assert want in names
 
@@ -39,7 +39,7 @@ def test_status_and_variant_strings(mha):
     assert lib.mha_status_string(99) == b"unknown status"
     for name, code in mha.VARIANTS.items():
         assert lib.mha_variant_name(code).decode() == name
-    assert lib.mha_version() >= 100
+    assert lib.mha_version() >= 101
 
 
 def _fwd(lib, q=0x1000, k=0x2000, v=0x3000, out=0x4000, lse=None, B=1, H=1, S=16, D=64,
@@ -96,3 +96,28 @@ def test_python_binding_rejects_cpu_tensors(mha):
     x = torch.zeros(1, 1, 16, 16, dtype=torch.float16)
     with pytest.raises(ValueError):
         mha.forward(x, x, x)
+
+
+def _bwd(lib, q=0x1000, k=0x2000, v=0x3000, out=0x4000, dout=0x5000, lse=0x6000, dq=0x7000,
+         dk=0x8000, dv=0x9000, delta=0xa000, B=1, H=1, S=16, D=64, causal=0, key_len=None,
+         dtype=1):
+    return lib.mha_backward(q, k, v, out, dout, lse, dq, dk, dv, delta, B, H, S, D, causal,
+                            key_len, dtype, None)
+
+
+def test_backward_validation_codes(mha):
+    lib = mha.load()
+    assert _bwd(lib, dout=None) == 1
+    assert _bwd(lib, lse=None) == 1
+    assert _bwd(lib, delta=None) == 1
+    assert _bwd(lib, dk=None) == 1
+    assert _bwd(lib, S=-1) == 2
+    assert _bwd(lib, S=1 << 26) == 2
+    assert _bwd(lib, D=48) == 3
+    assert _bwd(lib, dtype=0) == 3          # fp32 backward not provided
+    assert _bwd(lib, dtype=5) == 3
+    assert _bwd(lib, dv=0x9008) == 4
+    assert _bwd(lib, out=0x4004) == 4
+    assert _bwd(lib, delta=0xa002) == 4
+    assert _bwd(lib, B=0) == 0              # empty: no-op
+    assert _bwd(lib, S=0, dout=None) == 0

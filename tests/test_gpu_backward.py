@@ -1,0 +1,139 @@
+"""GPU parity of the backward pass: dq, dk, dv from the HIP kernels (through
+the C ABI binding, fed by the HIP forward's out and lse) against the float64
+oracle's gradients of the same inputs, element by element, under the same
+graded rule as the forward: |u-r| <= 2e-3 or |u-r| <= 2e-2 |r|."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import THREADS
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _inputs(B, H, S, D, dt, seed, key_len=None):
+    g = torch.Generator().manual_seed(seed)
+    q, k, v, do = (torch.randn(B, H, S, D, generator=g).to(DT[dt]) for _ in range(4))
+    kl = None if key_len is None else torch.tensor(key_len, dtype=torch.int32)
+    return q, k, v, do, kl
+
+
+def _run(mha, q, k, v, do, kl, causal):
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    kld = None if kl is None else kl.cuda()
+    out, lse = mha.forward(qd, kd, vd, causal=causal, key_len=kld)
+    dq, dk, dv = mha.backward(qd, kd, vd, out, lse, dod, causal=causal, key_len=kld)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def _check(got, q, k, v, do, kl, causal, label):
+    ref = oracle.attention_backward(q, k, v, do, causal=causal, key_len=kl, threads=THREADS)
+    worst = []
+    for name, u, r in zip(("dq", "dk", "dv"), got, ref):
+        ok = oracle.gate(u, r)
+        frac = oracle.budget_fraction(u, r)
+        worst.append(frac)
+        if not ok.all():
+            bad = np.argwhere(~ok)[:5].tolist()
+            raise AssertionError(f"{label}: {name}: {int((~ok).sum())} elements fail the rule "
+                                 f"(budget {frac:.3f}); first {bad}")
+    print(f"{label}: budget dq {worst[0]:.3f} dk {worst[1]:.3f} dv {worst[2]:.3f}", flush=True)
+    return worst
+
+
+SHAPES = [  # (B, H, S, D, key_len)
+    (1, 2, 64, 64, None),
+    (2, 2, 100, 32, [100, 37]),
+    (1, 3, 17, 16, None),
+    (2, 2, 130, 128, [130, 66]),
+    (1, 2, 96, 256, [96]),
+    (2, 1, 200, 64, [1, 200]),
+]
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s[:4])))
+def test_backward_shapes(mha, shape, causal, dt):
+    B, H, S, D, key_len = shape
+    q, k, v, do, kl = _inputs(B, H, S, D, dt, 7, key_len)
+    got = _run(mha, q, k, v, do, kl, causal)
+    _check(got, q, k, v, do, kl, causal, f"{shape} causal={causal} {dt}")
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_backward_seeds(mha, seed):
+    """The pages' backward workload shape reduced in batch (B=1, H=12,
+    S=1024, d_h=64, causal, bf16; rustingstudio "brain/docs/baseline",
+    "Fused attention"), over seeds."""
+    q, k, v, do, kl = _inputs(1, 12, 1024, 64, "bf16", seed)
+    got = _run(mha, q, k, v, do, kl, True)
+    _check(got, q, k, v, do, kl, True, f"bwd B=1 H=12 S=1024 seed {seed}")
+
+
+def test_backward_full_workload(mha):
+    """B=4, H=12, S=1024, d_h=64, causal, bf16, every element."""
+    q, k, v, do, kl = _inputs(4, 12, 1024, 64, "bf16", 0)
+    got = _run(mha, q, k, v, do, kl, True)
+    _check(got, q, k, v, do, kl, True, "bwd full workload")
+
+
+def test_backward_edges(mha):
+    # no visible key: every gradient is zero
+    q, k, v, do, _ = _inputs(2, 2, 40, 64, "f16", 3)
+    kl = torch.tensor([0, 40], dtype=torch.int32)
+    dq, dk, dv = _run(mha, q, k, v, do, kl, True)
+    assert not dq[0].any() and not dk[0].any() and not dv[0].any()
+    _check((dq, dk, dv), q, k, v, do, kl, True, "key_len 0")
+    # one row, one key
+    q, k, v, do, _ = _inputs(1, 1, 1, 32, "f16", 4)
+    got = _run(mha, q, k, v, do, None, False)
+    _check(got, q, k, v, do, None, False, "S=1")
+
+
+def test_backward_padding_never_read(mha):
+    """NaN in padded key / value rows changes nothing; padded keys get zero."""
+    q, k, v, do, _ = _inputs(1, 2, 90, 64, "f16", 5)
+    kl = torch.tensor([50], dtype=torch.int32)
+    base = _run(mha, q, k, v, do, kl, False)
+    kp, vp = k.clone(), v.clone()
+    kp[:, :, 50:] = float("nan")
+    vp[:, :, 50:] = float("nan")
+    pois = _run(mha, q, kp, vp, do, kl, False)
+    for a, b in zip(base, pois):
+        assert torch.equal(a, b)
+    assert not base[1][:, :, 50:].any() and not base[2][:, :, 50:].any()
+    _check(base, q, k, v, do, kl, False, "poisoned padding")
+
+
+def test_backward_deterministic(mha):
+    q, k, v, do, _ = _inputs(1, 2, 300, 64, "bf16", 6)
+    a = _run(mha, q, k, v, do, None, True)
+    b = _run(mha, q, k, v, do, None, True)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_backward_row_term_workspace(mha, dt):
+    """The workspace holds D: for fp16 rowsum(dout * out) of the forward's
+    rounded output, for bf16 rowsum(P * dP), i.e. dout . O of the exact
+    output (float64 oracle), to fp32 accumulation accuracy."""
+    q, k, v, do, _ = _inputs(1, 2, 300, 64, dt, 6)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    out, lse = mha.forward(qd, kd, vd, causal=True)
+    delta = torch.empty(lse.shape, dtype=torch.float32, device="cuda")
+    mha.backward(qd, kd, vd, out, lse, dod, causal=True, delta=delta)
+    torch.cuda.synchronize()
+    if dt == "f16":
+        ref = (dod.float() * out.float()).sum(-1).cpu().double().numpy()
+    else:
+        o64, _ = oracle.attention(q, k, v, causal=True)
+        ref = (do.double().numpy() * o64).sum(-1)
+    got = delta.cpu().double().numpy()
+    assert np.allclose(got, ref, rtol=1e-4, atol=1e-4), np.abs(got - ref).max()

@@ -34,11 +34,13 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, GB/s
 PEAK_MFMA_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}  # dense matrix-core peaks
 MALL_BYTES = 256 << 20           # working sets below this are rotated over buffer sets
 
-DEFAULT_STEPS = {"tiny": 2000, "launch": 2000, "bandwidth": 100, "compute": 200, "long": 4}
-DEFAULT_WARMUP = {"tiny": 50, "launch": 50, "bandwidth": 5, "compute": 10, "long": 1}
+DEFAULT_STEPS = {"tiny": 2000, "launch": 2000, "bandwidth": 100, "compute": 200, "long": 4,
+                 "bwd": 50}
+DEFAULT_WARMUP = {"tiny": 50, "launch": 50, "bandwidth": 5, "compute": 10, "long": 1, "bwd": 5}
 WARMUP_S = 0.5                   # minimum warm-up time before any timed region
-DEFAULT_GRAPH = {"tiny": 100, "launch": 100, "bandwidth": 0, "compute": 0, "long": 0}
-BOUND = {"tiny": "hbm", "launch": "hbm", "bandwidth": "hbm", "compute": "mfma", "long": "mfma"}
+DEFAULT_GRAPH = {"tiny": 100, "launch": 100, "bandwidth": 0, "compute": 0, "long": 0, "bwd": 0}
+BOUND = {"tiny": "hbm", "launch": "hbm", "bandwidth": "hbm", "compute": "mfma", "long": "mfma",
+         "bwd": "mfma"}
 KERNEL_SOURCES = ("attn_common.h", "attn_mfma.hip", "attn_short.hip", "attn_short16.hip",
                   "attn_f32.hip", "attn_valu.hip", "launch.h", "mha_api.hip")
 
@@ -139,6 +141,102 @@ def cpu_baseline(w, q, k, v, kl, flops_per_pair_unit: int, budget_s: float = 12.
             "host_cores_available": avail}
 
 
+def bench_backward(args, w, mha):
+    """One step = one mha_backward call (dq, dk, dv of sum(dout * out)) on
+    inputs resident in device memory, the forward's out / lse computed once
+    beforehand. FLOPs: 10 * d_h per visible pair (the five products S, dP,
+    dV, dQ, dK of 2 * d_h each)."""
+    import torch
+    import oracle
+    from workloads import make_backward_inputs
+
+    if w.dtype == torch.float32:
+        raise SystemExit("the backward takes fp16 / bf16 inputs")
+    K = args.steps if args.steps is not None else DEFAULT_STEPS.get(w.name, 20)
+    W = args.warmup if args.warmup is not None else DEFAULT_WARMUP.get(w.name, 3)
+    dev = torch.device("cuda:0")
+    q, k, v, kl, dout = make_backward_inputs(w, args.seed, device=dev)
+    kl_cpu = None if kl is None else kl.cpu()
+    pairs = pair_count(w, kl_cpu)
+    flops = 10 * w.D * pairs
+    out, lse = mha.forward(q, k, v, causal=w.causal, key_len=kl)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    delta = torch.empty_like(lse)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        mha.backward(q, k, v, out, lse, dout, causal=w.causal, key_len=kl,
+                     dq=dq, dk=dk, dv=dv, delta=delta, stream=stream)
+
+    t_w = time.perf_counter()
+    i = 0
+    while i < W or time.perf_counter() - t_w < WARMUP_S:
+        step()
+        i += 1
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(K):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = e0.elapsed_time(e1)
+    ms_per_step = max(ev_ms, wall * 1e3) / K
+    k_avg_ms = ev_ms / K
+    tag = dtype_tag(w.dtype)
+    achieved = flops / (k_avg_ms * 1e-3) / 1e12
+    peak = PEAK_MFMA_TFLOPS[tag]
+    res = {
+        "metric": "attention backward TFLOP/s (dq, dk, dv; 10*d_h flops per visible pair) "
+                  "and % of MI355X MFMA roofline",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 4),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": tag, "data": "synthetic",
+        "config": {"workload": w.name, "pass": "backward", "B": w.B, "H": w.H, "S": w.S,
+                   "d_h": w.D, "causal": w.causal,
+                   "key_len": (None if w.key_len is None else list(w.key_len)), "seed": args.seed,
+                   "kernels": "row-term pass (bf16 only), dq, dk/dv", "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 5), "traffic": None,
+            "kernel_avg_us": round(k_avg_ms * 1e3, 3),
+            "kernel_timing": "HIP events around the timed region / %d backward calls "
+                             "(all kernels of a call)" % K,
+            "algorithmic_flops": flops, "kernel_source_hash": kernel_source_hash(),
+        },
+        "flops_per_step": flops, "visible_pairs": pairs,
+    }
+    if not args.no_cpu_baseline:
+        # the float64 oracle's backward on the whole workload
+        avail = len(os.sched_getaffinity(0))
+        try:
+            from threadpoolctl import threadpool_info
+            blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        except Exception:
+            blas = 1
+        qc, kc, vc, dc = (t.cpu() for t in (q, k, v, dout))
+        reps = 0
+        t0 = time.perf_counter()
+        while True:  # the whole workload, repeated until about 12 s have passed
+            oracle.attention_backward(qc, kc, vc, dc, causal=w.causal, key_len=kl_cpu)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt > 12.0:
+                break
+        sample_flops = reps * flops
+        res["cpu_baseline"] = {"value": sample_flops / dt / 1e12, "unit": "TFLOP/s",
+                               "cores": blas, "kind": "oracle",
+                               "sample": f"whole workload, repeated x{reps}",
+                               "seconds": round(dt, 3), "host_cores_available": avail}
+    return res
+
+
 def copy_calibration(nbytes: int, reps: int):
     """A plain device copy of known size, for scaling the HBM byte counters."""
     import torch
@@ -156,8 +254,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="launch",
-                    choices=["tiny", "launch", "bandwidth", "compute", "long"])
+    ap.add_argument("--workload", default=None,
+                    choices=["tiny", "launch", "bandwidth", "compute", "long", "bwd"],
+                    help="default: launch for the forward, bwd for the backward")
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
+                    help="time the forward (default) or the backward (dq, dk, dv)")
     ap.add_argument("--variant", default="auto")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -184,7 +285,12 @@ def main():
     from workloads import WORKLOADS, make_inputs
 
     mha.load()  # raises if the HIP library is missing: there is no fallback
+    if args.workload is None:
+        args.workload = "bwd" if args.which == "bwd" else "launch"
     w = WORKLOADS[args.workload]
+    if args.which == "bwd":
+        print(json.dumps(bench_backward(args, w, mha)), flush=True)
+        return
     K = args.steps if args.steps is not None else DEFAULT_STEPS[w.name]
     W = args.warmup if args.warmup is not None else DEFAULT_WARMUP[w.name]
     dev = torch.device("cuda:0")

@@ -274,20 +274,31 @@ attn_bwd_dq(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restr
 
       // dQ^T += K^T dS^T, one key pair at a time
       if constexpr (MODE == kRowPass) continue;
+      // (transposed reads through inline asm, LA column tiles ahead, so the
+      // compiler does not make them wait for the next block's copy)
 #pragma unroll
       for (int p = 0; p < NKP; ++p) {
-        const T* kt0 = Ks + 32 * p * STR + trow;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const i16x4 a0 = lds_read_tr16(kt0 + 16 * dt);
-          const i16x4 a1 = lds_read_tr16(kt0 + 16 * STR + 16 * dt);
-          const T8 kf = __builtin_bit_cast(T8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+        const uint32_t ka = lds_addr(Ks + 32 * p * STR + trow);
+        constexpr int LA = NDT < 4 ? NDT : 4;
+        i16x4 a0[NDT], a1[NDT];
+        auto issue = [&](auto J) {
+          constexpr int j = decltype(J)::value;
+          a0[j] = lds_read_tr16_asm<16 * j * (int)sizeof(T)>(ka);
+          a1[j] = lds_read_tr16_asm<(16 * STR + 16 * j) * (int)sizeof(T)>(ka);
+        };
+        static_for<LA>(issue);
+        static_for<NDT>([&](auto DT) {
+          constexpr int dt = decltype(DT)::value;
+          if constexpr (dt + LA < NDT) issue(std::integral_constant<int, dt + LA>{});
+          constexpr int last = dt + LA < NDT ? dt + LA : NDT - 1;
+          lgkm_wait<2 * (last - dt)>(a0[dt], a1[dt]);
+          const T8 kf = __builtin_bit_cast(T8, __builtin_shufflevector(a0[dt], a1[dt], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int t = 0; t < NQT; ++t) {
             acc_dq[t][dt] = mfma_k32(kf, dsf[t][p], acc_dq[t][dt]);
             if constexpr (kBf16) acc_dq[t][dt] = mfma_k32(kf, dsl[t][p], acc_dq[t][dt]);
           }
-        }
+        });
       }
     }
   }
@@ -486,15 +497,26 @@ attn_bwd_dkv(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __rest
           }
         }
         // dV^T += dO^T P and dK^T += Q^T dS over the pair's 32 queries
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const int tb = 32 * p * STR + trow + 16 * dt;
-          const i16x4 o0 = lds_read_tr16(dOs + tb);
-          const i16x4 o1 = lds_read_tr16(dOs + tb + 16 * STR);
-          const i16x4 q0r = lds_read_tr16(Qs + tb);
-          const i16x4 q1r = lds_read_tr16(Qs + tb + 16 * STR);
-          const T8 oa = __builtin_bit_cast(T8, __builtin_shufflevector(o0, o1, 0, 1, 2, 3, 4, 5, 6, 7));
-          const T8 qa = __builtin_bit_cast(T8, __builtin_shufflevector(q0r, q1r, 0, 1, 2, 3, 4, 5, 6, 7));
+        // (transposed reads through inline asm, LA column tiles ahead)
+        const uint32_t oaddr = lds_addr(dOs + 32 * p * STR + trow);
+        const uint32_t qaddr = lds_addr(Qs + 32 * p * STR + trow);
+        constexpr int LA = NDT < 3 ? NDT : 3;
+        i16x4 o0[NDT], o1[NDT], q0r[NDT], q1r[NDT];
+        auto issue = [&](auto J) {
+          constexpr int j = decltype(J)::value;
+          o0[j] = lds_read_tr16_asm<16 * j * (int)sizeof(T)>(oaddr);
+          o1[j] = lds_read_tr16_asm<(16 * STR + 16 * j) * (int)sizeof(T)>(oaddr);
+          q0r[j] = lds_read_tr16_asm<16 * j * (int)sizeof(T)>(qaddr);
+          q1r[j] = lds_read_tr16_asm<(16 * STR + 16 * j) * (int)sizeof(T)>(qaddr);
+        };
+        static_for<LA>(issue);
+        static_for<NDT>([&](auto DT) {
+          constexpr int dt = decltype(DT)::value;
+          if constexpr (dt + LA < NDT) issue(std::integral_constant<int, dt + LA>{});
+          constexpr int last = dt + LA < NDT ? dt + LA : NDT - 1;
+          lgkm_wait<4 * (last - dt)>(o0[dt], o1[dt], q0r[dt], q1r[dt]);
+          const T8 oa = __builtin_bit_cast(T8, __builtin_shufflevector(o0[dt], o1[dt], 0, 1, 2, 3, 4, 5, 6, 7));
+          const T8 qa = __builtin_bit_cast(T8, __builtin_shufflevector(q0r[dt], q1r[dt], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int t = 0; t < NKTW; ++t) {
             adv[t][dt] = mfma_k32(oa, pf[t], adv[t][dt]);
@@ -504,7 +526,7 @@ attn_bwd_dkv(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __rest
               adk[t][dt] = mfma_k32(qa, dsl[t], adk[t][dt]);
             }
           }
-        }
+        });
       }
     }
   }
@@ -561,9 +583,16 @@ static hipError_t launch_bwd_one(const BwdParams& p, hipStream_t s) {
 template <typename T>
 static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
   switch (p.D) {
-    case 16: return launch_bwd_one<T, 16, 2, 4, 64, 2, 64>(p, s);
-    case 32: return launch_bwd_one<T, 32, 2, 4, 64, 2, 64>(p, s);
-    case 64: return launch_bwd_one<T, 64, 2, 4, 64, 2, 64>(p, s);
+    // (query tiles per wave, waves, keys per block | key tiles per wave,
+    // queries per block); one 16-row tile per wave doubles the workgroups,
+    // which the training shape (B=4, H=12, S=1024) needs, at no cost on
+    // larger problems; entries past 0 are kept for A/B measurement
+    case 16: return launch_bwd_one<T, 16, 1, 4, 64, 1, 64>(p, s);
+    case 32: return launch_bwd_one<T, 32, 1, 4, 64, 1, 64>(p, s);
+    case 64:
+      if (p.tile_cfg == 1) return launch_bwd_one<T, 64, 2, 4, 64, 2, 64>(p, s);
+      if (p.tile_cfg == 2) return launch_bwd_one<T, 64, 1, 8, 64, 1, 64>(p, s);
+      return launch_bwd_one<T, 64, 1, 4, 64, 1, 64>(p, s);
     case 128: return launch_bwd_one<T, 128, 1, 4, 64, 1, 64>(p, s);
     case 256: return launch_bwd_one<T, 256, 1, 4, 32, 1, 32>(p, s);
   }

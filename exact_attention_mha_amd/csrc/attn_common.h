@@ -95,6 +95,11 @@ __device__ __forceinline__ void lgkm_wait(i16x4& a, i16x4& b) {
   static_assert(N >= 0 && N < 16, "lgkmcnt range");
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
 }
+template <int N>
+__device__ __forceinline__ void lgkm_wait(i16x4& a, i16x4& b, i16x4& c, i16x4& d) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "i"(N));
+}
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }

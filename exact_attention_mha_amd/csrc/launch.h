@@ -42,6 +42,7 @@ struct BwdParams {
   int causal;
   int dtype;
   float c_log2;
+  int tile_cfg;            // tile-shape table entry (0 = default)
 };
 
 hipError_t launch_bwd(const BwdParams& p, hipStream_t s);          // dq then dk/dv kernel

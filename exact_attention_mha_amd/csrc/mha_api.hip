@@ -152,6 +152,7 @@ int mha_backward(const void* q, const void* k, const void* v, const void* out, c
   p.causal = causal ? 1 : 0;
   p.dtype = dtype;
   p.c_log2 = (float)(1.4426950408889634074 / sqrt((double)d_h));
+  p.tile_cfg = tile_config();
   const hipError_t e = mha::launch_bwd(p, (hipStream_t)stream);
   if (e == hipErrorInvalidConfiguration) return MHA_ERR_SHAPE;
   return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;

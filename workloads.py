@@ -8,7 +8,7 @@ thing the two sides share.
 The pages measure on an organiser harness that draws synthetic tensors from a
 fixed seed (devpost "gpu-transformer-optimization", "Development
 environment"); that harness and its shape list are not available, so these
-five workloads, with their stated shapes and distributions, stand in for it.
+workloads, with their stated shapes and distributions, stand in for it.
 
 Recipe (every workload): a torch CPU generator seeded with `seed` draws q, k,
 v in that order as float32 N(0, 1) tensors of shape [B, H, S, d_h], each then
@@ -26,7 +26,7 @@ from typing import Optional, Tuple
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "sample_rows"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_backward_inputs", "sample_rows"]
 
 
 @dataclass(frozen=True)
@@ -63,6 +63,11 @@ WORKLOADS = {
                         "MFMA-bound: d_model=1024 in 4 heads of 256"),
     "long": Workload("long", 32, 16, 100000, 64, torch.float16, True, ("fixed", 100000),
                      "long sequence: d_model=1024 in 16 heads of 64, S=100000"),
+    # the training shape of the fused backward on rustingstudio
+    # "brain/docs/baseline" ("Fused attention"): batch 4, sequence 1024,
+    # 12 heads of 64, causal, bf16 (one key/value head per query head here)
+    "bwd": Workload("bwd", 4, 12, 1024, 64, torch.bfloat16, True, None,
+                    "backward: B=4, S=1024, 12 heads of 64, causal, bf16"),
 }
 
 
@@ -100,6 +105,20 @@ def make_inputs(w: Workload, seed: int, device="cpu", gen_device: Optional[str] 
         del t
     kl = _draw_key_len(w, gen, device)
     return out[0], out[1], out[2], kl
+
+
+def make_backward_inputs(w: Workload, seed: int, device="cpu"):
+    """(q, k, v, key_len, dout): make_inputs, then the output gradient dout
+    drawn next from the same CPU generator, N(0, 1) in float32, cast to the
+    workload dtype."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(int(seed))
+    shape = (w.B, w.H, w.S, w.D)
+    qkv = [torch.randn(shape, generator=gen, dtype=torch.float32).to(w.dtype).to(device)
+           for _ in range(3)]
+    kl = _draw_key_len(w, gen, device)
+    dout = torch.randn(shape, generator=gen, dtype=torch.float32).to(w.dtype).to(device)
+    return qkv[0], qkv[1], qkv[2], kl, dout
 
 
 def sample_rows(B: int, H: int, S: int, n_rows: int, seed: int, tile: int = 128,

@@ -68,6 +68,8 @@ def load() -> ctypes.CDLL:
     lib.mha_forward.restype = ctypes.c_int
     lib.mha_forward_variant.argtypes = args + [ctypes.c_int]
     lib.mha_forward_variant.restype = ctypes.c_int
+    lib.mha_forward_strided.argtypes = [vp] * 6 + [i64] * 5 + [ctypes.c_int, vp, ctypes.c_int, vp]
+    lib.mha_forward_strided.restype = ctypes.c_int
     lib.mha_backward.argtypes = [vp] * 10 + [i64, i64, i64, i64, ctypes.c_int, vp, ctypes.c_int, vp]
     lib.mha_backward.restype = ctypes.c_int
     lib.mha_select_variant.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
@@ -105,10 +107,15 @@ def forward(q, k, v, causal: bool = False, key_len=None, out=None, lse=None,
     """softmax(Q K^T / sqrt(d_h) + mask) V on the GPU, plus per-row log-sum-exp.
 
     Args:
-      q, k, v: contiguous [B, H, S, d_h] GPU tensors of one dtype.
+      q, k, v: [B, H, S, d_h] GPU tensors of one dtype (k and v may have
+        H_kv heads, H_kv dividing H: grouped-query attention). Contiguous
+        tensors take mha_forward; strided views (last dimension contiguous,
+        e.g. [B, S, H, d_h] tensors transposed, or slices of a fused QKV
+        buffer) and grouped heads take mha_forward_strided (fp16 / bf16).
       causal: key j visible to query i only if j <= i.
       key_len: None (all S keys valid) or an int32 GPU tensor [B].
-      out: optional preallocated output (same shape/dtype as q).
+      out: optional preallocated output (shape/dtype of q; may be a strided
+        view whose last dimension is contiguous).
       lse: optional preallocated float32 [B, H, S]; ignored if return_lse is
         False and lse is None (then no lse is written).
       variant: kernel variant name (see VARIANTS); "auto" picks by regime.
@@ -119,22 +126,24 @@ def forward(q, k, v, causal: bool = False, key_len=None, out=None, lse=None,
     import torch
 
     lib = load()
-    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
-        raise ValueError(f"q, k, v must share a [B,H,S,d_h] shape, got {tuple(q.shape)}, "
-                         f"{tuple(k.shape)}, {tuple(v.shape)}")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError(f"q, k, v must be [B,H,S,d_h] / [B,H_kv,S,d_h] tensors, got "
+                         f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    B, H, S, D = q.shape
+    H_kv = k.shape[1]
+    if (k.shape[0], k.shape[2], k.shape[3]) != (B, S, D) or H_kv < 1 or H % H_kv:
+        raise ValueError(f"k, v must be [B, H_kv, S, d_h] with H_kv dividing H={H}, got "
+                         f"{tuple(k.shape)}")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    B, H, S, D = q.shape
     dcode = _dtype_code(q)
     if out is None:
-        out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda:
-        raise ValueError("out must be a contiguous GPU tensor shaped and typed like q")
+        out = torch.empty((B, H, S, D), dtype=q.dtype, device=q.device)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_cuda:
+        raise ValueError("out must be a GPU tensor shaped and typed like q")
     if lse is None and return_lse:
         lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     if lse is not None and (lse.shape != (B, H, S) or lse.dtype != torch.float32
@@ -149,6 +158,21 @@ def forward(q, k, v, causal: bool = False, key_len=None, out=None, lse=None,
     if variant not in VARIANTS:
         raise ValueError(f"unknown variant {variant!r}; one of {sorted(VARIANTS)}")
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    plain = H_kv == H and all(t.is_contiguous() for t in (q, k, v, out))
+    if not plain:
+        if variant != "auto":
+            raise ValueError("strided views and grouped heads take the automatic variant")
+        for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+            if t.stride(3) != 1:
+                raise ValueError(f"{name}: the d_h elements of a row must be contiguous")
+        strides = (ctypes.c_int64 * 12)(*[x for t in (q, k, v, out) for x in t.stride()[:3]])
+        status = lib.mha_forward_strided(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            lse.data_ptr() if lse is not None else None, strides,
+            B, H, H_kv, S, D, int(bool(causal)), kl_ptr, dcode, st.cuda_stream)
+        if status != 0:
+            raise MhaError("mha_forward_strided", status, lib.mha_status_string(status).decode())
+        return out, lse
     status = lib.mha_forward_variant(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
         lse.data_ptr() if lse is not None else None,

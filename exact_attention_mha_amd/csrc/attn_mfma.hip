@@ -58,7 +58,7 @@ template <typename T, int D, int NQT, int NW, int BK, bool SUM_MFMA, int NST>
 __global__ void __launch_bounds__(NW * 64, NW == 4 ? 2 : 1)
 attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
               T* __restrict__ Op, float* __restrict__ LSEp, const int32_t* __restrict__ key_len,
-              int H, int S, int causal, int n_qblk, float c_log2) {
+              int H, int S, int causal, int n_qblk, float c_log2, Layout lay) {
   typedef typename Vec<T>::x8 T8;
   typedef typename Vec<T>::x4 T4;
   constexpr int STR = D + 8;             // padded LDS row stride (elements)
@@ -71,7 +71,7 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   constexpr int NKT = BK / 16;           // key tiles per block
   constexpr int NKP = BK / 32;           // key pairs per block
   constexpr int NKC = D >= 32 ? D / 32 : 1;
-  constexpr int RB = D * (int)sizeof(T);  // bytes per row in memory
+  constexpr int ES = (int)sizeof(T);
   constexpr int BQ = NW * NQT * 16;
   constexpr bool kBf16 = __is_same(T, bf16_t);
   static_assert(BK % 32 == 0 && D % 16 == 0, "tile shape");
@@ -88,8 +88,16 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   int qb = (int)(logical - bh * (uint32_t)n_qblk);
   if (causal) qb = n_qblk - 1 - qb;  // heaviest causal tiles are dispatched first
   const int b = (int)(bh / (uint32_t)H);
+  const int h = (int)(bh - (uint32_t)b * (uint32_t)H);
   const int L = clamp_len(key_len, b, S);
-  const int64_t head = (int64_t)bh * S * D;
+  // this head's rows in each tensor, and the bytes between consecutive rows
+  const T* Qh = Qp + b * lay.q_b + h * lay.q_h;
+  const T* Kh = Kp + b * lay.k_b + (h / lay.group) * lay.k_h;
+  const T* Vh = Vp + b * lay.v_b + (h / lay.group) * lay.v_h;
+  T* Oh = Op + b * lay.o_b + h * lay.o_h;
+  const int RQ = lay.q_s * ES, RK = lay.k_s * ES, RV = lay.v_s * ES, RO = lay.o_s * ES;
+  // byte range of n rows starting at a head's first row
+  auto span = [](int n, int rs) { return (uint32_t)((n - 1) * rs + D * ES); };
 
   const int q_start = qb * BQ;
   const int q_end = min(S, q_start + BQ);
@@ -99,7 +107,7 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   const bool wave_live = wq0 < S;
   const int kend_w = !wave_live ? 0 : (causal ? min(L, min(q_end, wq0 + NQT * 16)) : L);
 
-  const rsrc_t ro = make_rsrc(Op + head, (uint32_t)S * RB);
+  const rsrc_t ro = make_rsrc(Oh, span(S, RO));
   const rsrc_t rl = make_rsrc(LSEp + (int64_t)bh * S, (uint32_t)S * 4);
 
   if (nblk == 0) {  // no visible key (L == 0): out = 0, lse = -inf
@@ -108,7 +116,7 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
       for (int t = 0; t < NQT; ++t) {
         const int row = wq0 + 16 * t + c;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) buf_store8(zero_vec<T4>(), ro, (row * D + 16 * dt + 4 * g) * 2);
+        for (int dt = 0; dt < NDT; ++dt) buf_store8(zero_vec<T4>(), ro, row * RO + (16 * dt + 4 * g) * 2);
         if (LSEp) buf_store4(-INFINITY, rl, g == 0 ? row * 4 : kOutOfRange);
       }
     }
@@ -116,8 +124,8 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   }
 
   // ---- per-lane DMA source offsets of this wave's slots (block relative)
-  const rsrc_t rk = make_rsrc(Kp + head, (uint32_t)kend * RB);
-  const rsrc_t rv = make_rsrc(Vp + head, (uint32_t)kend * RB);
+  const rsrc_t rk = make_rsrc(Kh, span(kend, RK));
+  const rsrc_t rv = make_rsrc(Vh, span(kend, RV));
   int koff[NIW], voff[NIW];
 #pragma unroll
   for (int i = 0; i < NIW; ++i) {
@@ -125,8 +133,8 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
     const int row = slot / SPR, j = slot - row * SPR;
     const bool live = slot < SLOTS && j < D / 8;
     const int base = 32 * (row >> 5);
-    koff[i] = live ? (base + k_key_of_row(row & 31)) * RB + 16 * j : kOutOfRange;
-    voff[i] = live ? (base + v_key_of_row(row & 31)) * RB + 16 * j : kOutOfRange;
+    koff[i] = live ? (base + k_key_of_row(row & 31)) * RK + 16 * j : kOutOfRange;
+    voff[i] = live ? (base + v_key_of_row(row & 31)) * RV + 16 * j : kOutOfRange;
   }
   auto dma_block = [&](int st, int k0) {
     T* Kst = smem + st * 2 * TILE;
@@ -135,24 +143,24 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
     for (int i = 0; i < NIW; ++i) {
       const int inst = wave + i * NW;
       if (NI % NW == 0 || inst < NI) {  // wave-uniform
-        dma16(rk, Kst + inst * 512, koff[i], k0 * RB);
-        dma16(rv, Vst + inst * 512, voff[i], k0 * RB);
+        dma16(rk, Kst + inst * 512, koff[i], k0 * RK);
+        dma16(rv, Vst + inst * 512, voff[i], k0 * RV);
       }
     }
   };
 
   // ---- Q fragments (rows past S read as zero)
-  const rsrc_t rq = make_rsrc(Qp + head, (uint32_t)S * RB);
+  const rsrc_t rq = make_rsrc(Qh, span(S, RQ));
   T8 qf[NQT][NKC];
   T4 qf4[NQT];
 #pragma unroll
   for (int t = 0; t < NQT; ++t) {
     const int row = wq0 + 16 * t + c;
     if constexpr (D == 16) {
-      qf4[t] = buf_load8<T4>(rq, (row * D + 4 * g) * 2, 0);
+      qf4[t] = buf_load8<T4>(rq, row * RQ + 4 * g * 2, 0);
     } else {
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) qf[t][kc] = buf_load16<T8>(rq, (row * D + 32 * kc + 8 * g) * 2, 0);
+      for (int kc = 0; kc < NKC; ++kc) qf[t][kc] = buf_load16<T8>(rq, row * RQ + (32 * kc + 8 * g) * 2, 0);
     }
   }
 
@@ -344,7 +352,7 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
         T4 ov;
 #pragma unroll
         for (int i = 0; i < 4; ++i) ov[i] = to_t<T>(o[t][dt][i] * inv);
-        buf_store8(ov, ro, (row * D + 16 * dt + 4 * g) * 2);
+        buf_store8(ov, ro, row * RO + (16 * dt + 4 * g) * 2);
       }
       if (LSEp) buf_store4((m_run[t] + fast_log2(l)) * kLn2, rl, g == 0 ? row * 4 : kOutOfRange);
     }
@@ -359,7 +367,7 @@ static hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((attn_fwd_mfma<T, D, NQT, NW, BK, SM, NST>), dim3((unsigned)n_wg), dim3(NW * 64), 0, s,
                      (const T*)p.q, (const T*)p.k, (const T*)p.v, (T*)p.out, p.lse, p.key_len,
-                     p.H, p.S, p.causal, n_qblk, p.c_log2);
+                     p.H, p.S, p.causal, n_qblk, p.c_log2, p.lay);
   return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ template <typename T, int QPW, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2)
 attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
                  T* __restrict__ Op, float* __restrict__ LSEp, const int32_t* __restrict__ key_len,
-                 int BH, int H, int S, float c_log2) {
+                 int BH, int H, int S, float c_log2, Layout lay) {
   constexpr bool causal = CAUSAL;
   typedef typename Vec<T>::x4 T4;
   constexpr int D = 16;
@@ -49,13 +49,16 @@ attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __
   const int item = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
   const int bh = item / PARTS, part = item - bh * PARTS;
   if (bh >= BH) return;  // wave-uniform; no barriers in this kernel
-  const int b = bh / H;
+  const int b = bh / H, h = bh - b * H;
   const int L = clamp_len(key_len, b, S);
-  const int64_t head = (int64_t)bh * S * D;
-  const rsrc_t rq = make_rsrc(Qp + head, (uint32_t)S * RB);
-  const rsrc_t rk = make_rsrc(Kp + head, (uint32_t)L * RB);
-  const rsrc_t rv = make_rsrc(Vp + head, (uint32_t)L * RB);
-  const rsrc_t ro = make_rsrc(Op + head, (uint32_t)S * RB);
+  // this head's rows in each tensor and the bytes between rows (a range of
+  // n rows covers (n - 1) row strides plus one row; none when n = 0)
+  const int RQ = lay.q_s * 2, RK = lay.k_s * 2, RV = lay.v_s * 2, RO = lay.o_s * 2;
+  auto span = [](int n, int rs) { return n > 0 ? (uint32_t)((n - 1) * rs + RB) : 0u; };
+  const rsrc_t rq = make_rsrc(Qp + b * lay.q_b + h * lay.q_h, span(S, RQ));
+  const rsrc_t rk = make_rsrc(Kp + b * lay.k_b + (h / lay.group) * lay.k_h, span(L, RK));
+  const rsrc_t rv = make_rsrc(Vp + b * lay.v_b + (h / lay.group) * lay.v_h, span(L, RV));
+  const rsrc_t ro = make_rsrc(Op + b * lay.o_b + h * lay.o_h, span(S, RO));
   const rsrc_t rl = make_rsrc(LSEp + (int64_t)bh * S, (uint32_t)S * 4);
 
   // query tiles of this wave; with pairs, wave `part` takes tiles part and
@@ -76,13 +79,13 @@ attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __
   // ---- operands straight from memory (keys past L and rows past S read 0)
   T4 qf[QPW], kf[NT], vt[NT];
 #pragma unroll
-  for (int j = 0; j < QPW; ++j) qf[j] = buf_load8<T4>(rq, (16 * tile[j] + c) * RB + 8 * g, 0);
+  for (int j = 0; j < QPW; ++j) qf[j] = buf_load8<T4>(rq, (16 * tile[j] + c) * RQ + 8 * g, 0);
   T4 vraw[NT];
 #pragma unroll
   for (int kt = 0; kt < NT; ++kt) {
     if (kt < kt_need) {
-      kf[kt] = buf_load8<T4>(rk, (16 * kt + c) * RB + 8 * g, 0);
-      vraw[kt] = buf_load8<T4>(rv, (16 * kt + c) * RB + 8 * g, 0);
+      kf[kt] = buf_load8<T4>(rk, (16 * kt + c) * RK + 8 * g, 0);
+      vraw[kt] = buf_load8<T4>(rv, (16 * kt + c) * RV + 8 * g, 0);
     }
   }
   T4 ident, ones;
@@ -118,7 +121,7 @@ attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __
     if (16 * t >= S) return;  // wave-uniform
     const int row = 16 * t + c;
     if (L == 0) {  // no visible key
-      buf_store8(zero_vec<T4>(), ro, row * RB + 8 * g);
+      buf_store8(zero_vec<T4>(), ro, row * RO + 8 * g);
       if (LSEp) buf_store4(-INFINITY, rl, g == 0 ? row * 4 : kOutOfRange);
       return;
     }
@@ -164,7 +167,7 @@ attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __
     T4 ov;
 #pragma unroll
     for (int i = 0; i < 4; ++i) ov[i] = to_t<T>(o[i] * inv);
-    buf_store8(ov, ro, row * RB + 8 * g);  // O^T lane layout: row, columns 4g..4g+3
+    buf_store8(ov, ro, row * RO + 8 * g);  // O^T lane layout: row, columns 4g..4g+3
     if (LSEp) buf_store4((m + fast_log2(l)) * kLn2, rl, g == 0 ? row * 4 : kOutOfRange);
     __builtin_amdgcn_sched_barrier(0);  // keep query tiles from interleaving (register pressure)
   };
@@ -182,11 +185,11 @@ static hipError_t launch_one_short16(const AttnParams& p, hipStream_t s) {
   if (p.causal)
     hipLaunchKernelGGL((attn_fwd_short16<T, QPW, true>), dim3((unsigned)n_wg), dim3(256), 0, s,
                        (const T*)p.q, (const T*)p.k, (const T*)p.v, (T*)p.out, p.lse, p.key_len,
-                       p.B * p.H, p.H, p.S, p.c_log2);
+                       p.B * p.H, p.H, p.S, p.c_log2, p.lay);
   else
     hipLaunchKernelGGL((attn_fwd_short16<T, QPW, false>), dim3((unsigned)n_wg), dim3(256), 0, s,
                        (const T*)p.q, (const T*)p.k, (const T*)p.v, (T*)p.out, p.lse, p.key_len,
-                       p.B * p.H, p.H, p.S, p.c_log2);
+                       p.B * p.H, p.H, p.S, p.c_log2, p.lay);
   return hipGetLastError();
 }
 

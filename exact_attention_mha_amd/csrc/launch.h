@@ -10,6 +10,22 @@
 
 namespace mha {
 
+// Where the rows of one (batch, head) start, per tensor: element offsets
+// b * *_b + h * *_h (k / v use head h / group), and element strides *_s
+// between consecutive rows; the d_h elements of a row are contiguous. The
+// contiguous [B, H, S, d_h] layout is *_b = H*S*d_h, *_h = S*d_h,
+// *_s = d_h, group = 1.
+struct Layout {
+  int64_t q_b, q_h, k_b, k_h, v_b, v_h, o_b, o_h;
+  int q_s, k_s, v_s, o_s;
+  int group;  // query heads per key/value head
+};
+
+inline Layout contiguous_layout(int H, int S, int D) {
+  const int64_t hs = (int64_t)S * D, bs = (int64_t)H * hs;
+  return Layout{bs, hs, bs, hs, bs, hs, bs, hs, D, D, D, D, 1};
+}
+
 struct AttnParams {
   const void* q;
   const void* k;
@@ -22,6 +38,7 @@ struct AttnParams {
   int dtype;               // enum mha_dtype
   float c_log2;            // log2(e) / sqrt(d_h)
   int tile_cfg;            // tile-shape table entry (0 = default)
+  Layout lay;              // strides (contiguous unless from mha_forward_strided)
 };
 
 // Backward: dq, dk, dv of sum(dout * out); delta is the caller's float

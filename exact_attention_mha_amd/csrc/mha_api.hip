@@ -99,6 +99,7 @@ int mha_forward_variant(const void* q, const void* k, const void* v, void* out, 
   p.dtype = dtype;
   p.c_log2 = (float)(1.4426950408889634074 / sqrt((double)d_h));
   p.tile_cfg = tile_config();
+  p.lay = mha::contiguous_layout((int)H, (int)S, (int)d_h);
 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipErrorInvalidValue;
@@ -108,6 +109,55 @@ int mha_forward_variant(const void* q, const void* k, const void* v, void* out, 
     case MHA_VARIANT_MFMA_SMALL: e = mha::launch_mfma_small(p, s); break;
     case MHA_VARIANT_VALU_D16: e = mha::launch_valu_d16(p, s); break;
     case MHA_VARIANT_SHORT: e = d_h == 16 ? mha::launch_short16(p, s) : mha::launch_short(p, s); break;
+  }
+  if (e == hipErrorInvalidConfiguration) return MHA_ERR_SHAPE;
+  return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
+}
+
+int mha_forward_strided(const void* q, const void* k, const void* v, void* out, float* lse,
+                        const int64_t* strides, int64_t B, int64_t H, int64_t H_kv, int64_t S,
+                        int64_t d_h, int causal, const int32_t* key_len, int dtype, void* stream) {
+  const int st = validate(q, k, v, out, lse, B, H, S, d_h, key_len, dtype);
+  if (st != MHA_OK) return st;
+  if (dtype == MHA_F32) return MHA_ERR_UNSUPPORTED;
+  if (H_kv <= 0 || H % H_kv != 0) return H_kv < 0 ? MHA_ERR_SHAPE : (H == 0 ? MHA_OK : MHA_ERR_SHAPE);
+  if (B == 0 || H == 0 || S == 0) return MHA_OK;
+  if (!strides) return MHA_ERR_NULL;
+  const int64_t esize = 2;
+  for (int t = 0; t < 4; ++t) {
+    const int64_t sb = strides[3 * t], sh = strides[3 * t + 1], ss = strides[3 * t + 2];
+    if (sb < 0 || sh < 0 || ss < d_h) return MHA_ERR_SHAPE;
+    if ((sb * esize) % 16 || (sh * esize) % 16 || (ss * esize) % 16) return MHA_ERR_MISALIGNED;
+    if (((S - 1) * ss + d_h) * esize >= ((int64_t)1 << 31)) return MHA_ERR_SHAPE;
+  }
+  int variant = choose(B, H, S, d_h, dtype);
+  if (variant == MHA_VARIANT_SHORT && d_h != 16)  // the d_h 32/64 short kernel is contiguous only
+    variant = B * H * ((S + 127) / 128) < 512 ? MHA_VARIANT_MFMA_SMALL : MHA_VARIANT_MFMA;
+
+  mha::AttnParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.key_len = key_len;
+  p.B = (int)B;
+  p.H = (int)H;
+  p.S = (int)S;
+  p.D = (int)d_h;
+  p.causal = causal ? 1 : 0;
+  p.dtype = dtype;
+  p.c_log2 = (float)(1.4426950408889634074 / sqrt((double)d_h));
+  p.tile_cfg = tile_config();
+  p.lay = mha::Layout{strides[0], strides[1], strides[3], strides[4], strides[6], strides[7],
+                      strides[9], strides[10], (int)strides[2], (int)strides[5], (int)strides[8],
+                      (int)strides[11], (int)(H / H_kv)};
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipErrorInvalidValue;
+  switch (variant) {
+    case MHA_VARIANT_MFMA: e = mha::launch_mfma(p, s); break;
+    case MHA_VARIANT_MFMA_SMALL: e = mha::launch_mfma_small(p, s); break;
+    case MHA_VARIANT_SHORT: e = mha::launch_short16(p, s); break;
   }
   if (e == hipErrorInvalidConfiguration) return MHA_ERR_SHAPE;
   return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
@@ -190,6 +240,6 @@ const char* mha_status_string(int status) {
   return "unknown status";
 }
 
-int mha_version(void) { return 101; }
+int mha_version(void) { return 102; }
 
 }  // extern "C"

@@ -106,6 +106,33 @@ int mha_forward_variant(const void* q, const void* k, const void* v, void* out, 
                         const int32_t* key_len, int dtype, void* stream, int variant);
 
 /*
+ * mha_forward_strided -- mha_forward over strided views, with grouped
+ * key / value heads.
+ *
+ * Removes the head-split copies of a layer that keeps q, k, v in one fused
+ * buffer or in [B, S, H, d_h] order: every tensor is indexed [b, h, i, d]
+ * through element strides, and the d_h elements of a row are contiguous.
+ *
+ *   strides  host pointer to 12 int64: the (batch, head, row) element
+ *            strides of q, k, v and out, in that order. Each must be
+ *            >= 0 and a multiple of 16 bytes; row strides >= d_h; one
+ *            head's rows must span < 2^31 bytes.
+ *   H_kv     key / value heads (>= 1, dividing H): query head h uses key /
+ *            value head h / (H / H_kv) (grouped-query attention; H_kv = H
+ *            is ordinary multi-head attention). k and v are indexed with
+ *            heads 0 .. H_kv - 1.
+ *   lse      NULL or contiguous fp32 [B, H, S], as for mha_forward.
+ *   other arguments as for mha_forward; dtype must be MHA_F16 or MHA_BF16.
+ *
+ * The rows of out written by one call must not overlap each other or any
+ * input. Returns an enum mha_status code; MHA_ERR_MISALIGNED for a stride
+ * or pointer that is not 16-byte aligned.
+ */
+int mha_forward_strided(const void* q, const void* k, const void* v, void* out, float* lse,
+                        const int64_t* strides, int64_t B, int64_t H, int64_t H_kv, int64_t S,
+                        int64_t d_h, int causal, const int32_t* key_len, int dtype, void* stream);
+
+/*
  * mha_backward -- enqueue the gradients of the forward above on `stream`.
  *
  * Given the output gradient dout of a loss, writes dq, dk, dv: the
@@ -148,7 +175,8 @@ const char* mha_variant_name(int variant);
 /* Static description of a status code. */
 const char* mha_status_string(int status);
 
-/* Library ABI version (major * 100 + minor); 101 adds mha_backward. */
+/* Library ABI version (major * 100 + minor); 101 adds mha_backward, 102
+ * mha_forward_strided. */
 int mha_version(void);
 
 #ifdef __cplusplus

@@ -121,3 +121,31 @@ def test_backward_validation_codes(mha):
     assert _bwd(lib, delta=0xa002) == 4
     assert _bwd(lib, B=0) == 0              # empty: no-op
     assert _bwd(lib, S=0, dout=None) == 0
+
+
+def _strided(lib, strides=None, B=1, H=4, H_kv=2, S=16, D=64, dtype=1, q=0x1000):
+    import ctypes
+    if strides is None:
+        strides = [H * S * D, S * D, D] * 4
+    arr = (ctypes.c_int64 * 12)(*strides)
+    return lib.mha_forward_strided(q, 0x2000, 0x3000, 0x4000, None, arr, B, H, H_kv, S, D, 0,
+                                   None, dtype, None)
+
+
+def test_strided_validation_codes(mha):
+    lib = mha.load()
+    assert _strided(lib, H_kv=3) == 2          # H_kv must divide H
+    assert _strided(lib, H_kv=0) == 2
+    assert _strided(lib, dtype=0) == 3         # fp16 / bf16 only
+    assert _strided(lib, D=48) == 3
+    assert _strided(lib, q=None) == 1
+    s = [4 * 16 * 64, 16 * 64, 64] * 4
+    bad = list(s); bad[2] = 32                 # row stride below d_h
+    assert _strided(lib, bad) == 2
+    bad = list(s); bad[5] = 68                 # k row stride not a multiple of 16 bytes
+    assert _strided(lib, bad) == 4
+    bad = list(s); bad[10] = -64               # negative head stride
+    assert _strided(lib, bad) == 2
+    bad = list(s); bad[8] = 1 << 27            # one head spans >= 2^31 bytes
+    assert _strided(lib, bad) == 2
+    assert _strided(lib, B=0) == 0

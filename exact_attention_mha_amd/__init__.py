@@ -72,6 +72,8 @@ def load() -> ctypes.CDLL:
     lib.mha_forward_strided.restype = ctypes.c_int
     lib.mha_backward.argtypes = [vp] * 10 + [i64, i64, i64, i64, ctypes.c_int, vp, ctypes.c_int, vp]
     lib.mha_backward.restype = ctypes.c_int
+    lib.mha_backward_grouped.argtypes = [vp] * 10 + [i64] * 5 + [ctypes.c_int, vp, ctypes.c_int, vp]
+    lib.mha_backward_grouped.restype = ctypes.c_int
     lib.mha_select_variant.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
     lib.mha_select_variant.restype = ctypes.c_int
     lib.mha_variant_name.argtypes = [ctypes.c_int]
@@ -187,10 +189,11 @@ def backward(q, k, v, out, lse, dout, causal: bool = False, key_len=None,
     """Gradients (dq, dk, dv) of sum(dout * out) through the attention forward.
 
     Args:
-      q, k, v, causal, key_len: exactly as passed to forward().
+      q, k, v, causal, key_len: exactly as passed to forward(); all
+        contiguous here, k and v with H or H_kv (dividing H) heads.
       out, lse: forward()'s outputs for those inputs (lse is required).
       dout: the output gradient, contiguous [B, H, S, d_h], dtype of q.
-      dq, dk, dv: optional preallocated outputs shaped and typed like q.
+      dq, dk, dv: optional preallocated outputs shaped like q, k, v.
       delta: optional float32 [B, H, S] workspace; receives rowsum(dout * out).
       stream: a torch.cuda.Stream (default: the current stream).
     Returns:
@@ -200,19 +203,25 @@ def backward(q, k, v, out, lse, dout, causal: bool = False, key_len=None,
 
     lib = load()
     B, H, S, D = q.shape
-    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous GPU tensor shaped and typed like q")
+    H_kv = k.shape[1] if k.dim() == 4 else -1
+    if H_kv < 1 or H % H_kv or k.shape != (B, H_kv, S, D) or v.shape != k.shape:
+        raise ValueError(f"k, v must be [B, H_kv, S, d_h] with H_kv dividing H={H}")
+    for name, t, shp in (("q", q, q.shape), ("k", k, k.shape), ("v", v, k.shape),
+                         ("out", out, q.shape), ("dout", dout, q.shape)):
+        if t.shape != shp or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor of shape {tuple(shp)} "
+                             f"and the dtype of q")
     if (lse is None or lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_cuda
             or not lse.is_contiguous()):
         raise ValueError("lse must be forward()'s contiguous float32 GPU tensor [B, H, S]")
     dcode = _dtype_code(q)
     grads = []
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
         if t is None:
-            t = torch.empty_like(q)
-        elif t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous GPU tensor shaped and typed like q")
+            t = torch.empty_like(like)
+        elif (t.shape != like.shape or t.dtype != q.dtype or not t.is_cuda
+              or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous GPU tensor shaped like its input")
         grads.append(t)
     if delta is None:
         delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
@@ -226,10 +235,10 @@ def backward(q, k, v, out, lse, dout, causal: bool = False, key_len=None,
             raise ValueError("key_len must be a contiguous int32 GPU tensor [B]")
         kl_ptr = key_len.data_ptr()
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
-    status = lib.mha_backward(
+    status = lib.mha_backward_grouped(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
         lse.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
-        delta.data_ptr(), B, H, S, D, int(bool(causal)), kl_ptr, dcode, st.cuda_stream)
+        delta.data_ptr(), B, H, H_kv, S, D, int(bool(causal)), kl_ptr, dcode, st.cuda_stream)
     if status != 0:
-        raise MhaError("mha_backward", status, lib.mha_status_string(status).decode())
+        raise MhaError("mha_backward_grouped", status, lib.mha_status_string(status).decode())
     return tuple(grads)

@@ -101,7 +101,7 @@ __global__ void __launch_bounds__(NW * 64, 2)
 attn_bwd_dq(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
             const T* __restrict__ Op, const T* __restrict__ dOp, const float* __restrict__ LSEp,
             T* __restrict__ dQp, float* __restrict__ Dp, const int32_t* __restrict__ key_len,
-            int H, int S, int causal, int n_qblk, float c_log2, float scale) {
+            int H, int S, int causal, int n_qblk, float c_log2, float scale, int group) {
   typedef typename Vec<T>::x8 T8;
   typedef typename Vec<T>::x4 T4;
   typedef BwdTile<T, D, BK, NW> Tile;
@@ -128,6 +128,9 @@ attn_bwd_dq(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restr
   const int b = (int)(bh / (uint32_t)H);
   const int L = clamp_len(key_len, b, S);
   const int64_t head = (int64_t)bh * S * D;
+  // key / value head of this query head (grouped-query attention)
+  const int hk = (int)(bh - (uint32_t)b * (uint32_t)H) / group;
+  const int64_t head_kv = ((int64_t)b * (H / group) + hk) * S * D;
   const int q_start = qb * BQ;
   const int q_end = min(S, q_start + BQ);
   const int kend = causal ? min(L, q_end) : L;
@@ -192,8 +195,8 @@ attn_bwd_dq(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restr
     for (int dt = 0; dt < NDT; ++dt) acc_dq[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (nblk > 0) {
-    const rsrc_t rk = make_rsrc(Kp + head, (uint32_t)kend * RB);
-    const rsrc_t rv = make_rsrc(Vp + head, (uint32_t)kend * RB);
+    const rsrc_t rk = make_rsrc(Kp + head_kv, (uint32_t)kend * RB);
+    const rsrc_t rv = make_rsrc(Vp + head_kv, (uint32_t)kend * RB);
     int off[Tile::NIW];
     Tile::offsets(wave, lane, off);
     auto dma_block = [&](int st, int k0) {
@@ -334,7 +337,7 @@ __global__ void __launch_bounds__(NW * 64, 2)
 attn_bwd_dkv(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
              const T* __restrict__ dOp, const float* __restrict__ LSEp, const float* __restrict__ Dp,
              T* __restrict__ dKp, T* __restrict__ dVp, const int32_t* __restrict__ key_len,
-             int H, int S, int causal, int n_kblk, float c_log2, float scale) {
+             int H, int S, int causal, int n_kblk, float c_log2, float scale, int group) {
   typedef typename Vec<T>::x8 T8;
   typedef typename Vec<T>::x4 T4;
   typedef BwdTile<T, D, BQb, NW> Tile;
@@ -356,12 +359,17 @@ attn_bwd_dkv(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __rest
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
 
+  // one workgroup per (batch, key / value head, key block); it walks the
+  // query blocks of every query head of the group, so the key / value
+  // gradients of grouped-query attention are complete without atomics
+  const int Hk = H / group;
   const uint32_t logical = xcd_logical_id(blockIdx.x, gridDim.x);
-  const uint32_t bh = logical / (uint32_t)n_kblk;
+  const uint32_t bh = logical / (uint32_t)n_kblk;  // over B * Hk
   const int kb = (int)(logical - bh * (uint32_t)n_kblk);
-  const int b = (int)(bh / (uint32_t)H);
+  const int b = (int)(bh / (uint32_t)Hk);
   const int L = clamp_len(key_len, b, S);
-  const int64_t head = (int64_t)bh * S * D;
+  const int64_t head = (int64_t)bh * S * D;        // K, V, dK, dV
+  const int64_t bhq0 = (int64_t)b * H + (int64_t)(bh - (uint32_t)b * (uint32_t)Hk) * group;
   const int k_start = kb * BKW;
   const int wk0 = k_start + wave * NKTW * 16;
   const rsrc_t rdk = make_rsrc(dKp + head, (uint32_t)S * RB);
@@ -370,7 +378,7 @@ attn_bwd_dkv(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __rest
   // queries that see any key of the workgroup: all when not causal, else
   // from its first visible key on; none past the key length
   const int q_lo = causal ? min(k_start, L) / BQb * BQb : 0;
-  const int nblk = k_start >= L ? 0 : (S - q_lo + BQb - 1) / BQb;
+  const int nblk = k_start >= L ? 0 : (S - q_lo + BQb - 1) / BQb;  // per query head
 
   // ---- K and V fragments (B operands, key column c) for this wave's tiles
   const rsrc_t rk = make_rsrc(Kp + head, (uint32_t)L * RB);
@@ -400,16 +408,21 @@ attn_bwd_dkv(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __rest
     for (int dt = 0; dt < NDT; ++dt) adk[t][dt] = adv[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (nblk > 0) {
-    const rsrc_t rq = make_rsrc(Qp + head, (uint32_t)S * RB);
-    const rsrc_t rdo = make_rsrc(dOp + head, (uint32_t)S * RB);
-    const rsrc_t rl = make_rsrc(LSEp + (int64_t)bh * S, (uint32_t)S * 4);
-    const rsrc_t rd = make_rsrc(Dp + (int64_t)bh * S, (uint32_t)S * 4);
     int off[Tile::NIW];
     Tile::offsets(wave, lane, off);
     // row vectors (lse, D of the block's rows): lane i of wave 0 copies one
     // float of each; lanes past the block (and rows past S) write zeros
     const int voff = lane < BQb ? 4 * lane : kOutOfRange;
-    auto dma_block = [&](int st, int q0) {
+    // iteration it covers query head j = it / nblk of the group, query
+    // block it % nblk
+    auto dma_block = [&](int st, int it) {
+      const int j = it / nblk;
+      const int q0 = q_lo + (it - j * nblk) * BQb;
+      const int64_t hq = (bhq0 + j) * S * D, hr = (bhq0 + j) * S;
+      const rsrc_t rq = make_rsrc(Qp + hq, (uint32_t)S * RB);
+      const rsrc_t rdo = make_rsrc(dOp + hq, (uint32_t)S * RB);
+      const rsrc_t rl = make_rsrc(LSEp + hr, (uint32_t)S * 4);
+      const rsrc_t rd = make_rsrc(Dp + hr, (uint32_t)S * 4);
       T* Qst = smem + st * 2 * Tile::ELEMS;
       Tile::copy(rq, Qst, off, wave, q0 * RB);
       Tile::copy(rdo, Qst + Tile::ELEMS, off, wave, q0 * RB);
@@ -418,20 +431,22 @@ attn_bwd_dkv(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __rest
         dma4(rd, svec + st * 2 * ROWF + ROWF, voff, q0 * 4);
       }
     };
-    dma_block(0, q_lo);
+    dma_block(0, 0);
 
     const int rrow = bwd_lds_row(c) * STR;
     const int trow = bwd_lds_row(4 * g + (c >> 2)) * STR + 4 * (c & 3);
 
-    for (int qb = 0; qb < nblk; ++qb) {
+    const int n_it = group * nblk;
+    for (int it = 0; it < n_it; ++it) {
+      const int qb = it - (it / nblk) * nblk;
       const int q0 = q_lo + qb * BQb;
       wait_vmem();
       block_barrier();
-      if (qb + 1 < nblk) dma_block((qb + 1) & 1, q0 + BQb);
+      if (it + 1 < n_it) dma_block((it + 1) & 1, it + 1);
 
-      const T* Qs = smem + (qb & 1) * 2 * Tile::ELEMS;
+      const T* Qs = smem + (it & 1) * 2 * Tile::ELEMS;
       const T* dOs = Qs + Tile::ELEMS;
-      const float* ls = svec + (qb & 1) * 2 * ROWF;
+      const float* ls = svec + (it & 1) * 2 * ROWF;
       const float* ds = ls + ROWF;
       // a block needs masking if it reaches past S, or (causal) has a
       // query before some key of this wave
@@ -557,26 +572,26 @@ static hipError_t launch_bwd_one(const BwdParams& p, hipStream_t s) {
   constexpr int BKW = NW * NKTW * 16;
   const int n_qblk = (p.S + BQ - 1) / BQ;
   const int n_kblk = (p.S + BKW - 1) / BKW;
-  const int64_t wq = (int64_t)p.B * p.H * n_qblk, wk = (int64_t)p.B * p.H * n_kblk;
+  const int64_t wq = (int64_t)p.B * p.H * n_qblk, wk = (int64_t)p.B * (p.H / p.group) * n_kblk;
   if (wq > 0x7fffffffLL || wk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const float scale = 1.f / sqrtf((float)p.D);
   constexpr bool kBf16 = __is_same(T, bf16_t);
   if constexpr (kBf16) {
     hipLaunchKernelGGL((attn_bwd_dq<T, D, NQT, NW, BK, kRowPass>), dim3((unsigned)wq), dim3(NW * 64), 0, s,
                        (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.out, (const T*)p.dout,
-                       p.lse, (T*)p.dq, p.delta, p.key_len, p.H, p.S, p.causal, n_qblk, p.c_log2, scale);
+                       p.lse, (T*)p.dq, p.delta, p.key_len, p.H, p.S, p.causal, n_qblk, p.c_log2, scale, p.group);
     hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;
   }
   constexpr int kDqMode = kBf16 ? kRowRead : kRowFromOut;
   hipLaunchKernelGGL((attn_bwd_dq<T, D, NQT, NW, BK, kDqMode>), dim3((unsigned)wq), dim3(NW * 64), 0, s,
                      (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.out, (const T*)p.dout,
-                     p.lse, (T*)p.dq, p.delta, p.key_len, p.H, p.S, p.causal, n_qblk, p.c_log2, scale);
+                     p.lse, (T*)p.dq, p.delta, p.key_len, p.H, p.S, p.causal, n_qblk, p.c_log2, scale, p.group);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_bwd_dkv<T, D, NKTW, NW, BQb>), dim3((unsigned)wk), dim3(NW * 64), 0, s,
                      (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.dout, p.lse, p.delta,
-                     (T*)p.dk, (T*)p.dv, p.key_len, p.H, p.S, p.causal, n_kblk, p.c_log2, scale);
+                     (T*)p.dk, (T*)p.dv, p.key_len, p.H, p.S, p.causal, n_kblk, p.c_log2, scale, p.group);
   return hipGetLastError();
 }
 

@@ -60,6 +60,7 @@ struct BwdParams {
   int dtype;
   float c_log2;
   int tile_cfg;            // tile-shape table entry (0 = default)
+  int group;               // query heads per key / value head (k, v, dk, dv have H / group)
 };
 
 hipError_t launch_bwd(const BwdParams& p, hipStream_t s);          // dq then dk/dv kernel

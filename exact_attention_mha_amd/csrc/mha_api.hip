@@ -170,13 +170,14 @@ int mha_forward(const void* q, const void* k, const void* v, void* out, float* l
                              MHA_VARIANT_AUTO);
 }
 
-int mha_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                 const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t B,
-                 int64_t H, int64_t S, int64_t d_h, int causal, const int32_t* key_len, int dtype,
-                 void* stream) {
+int mha_backward_grouped(const void* q, const void* k, const void* v, const void* out,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         float* delta, int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t d_h,
+                         int causal, const int32_t* key_len, int dtype, void* stream) {
   int st = validate(q, k, v, dq, lse, B, H, S, d_h, key_len, dtype);
   if (st != MHA_OK) return st;
   if (dtype == MHA_F32) return MHA_ERR_UNSUPPORTED;
+  if (H_kv <= 0 || (H > 0 && H % H_kv != 0)) return MHA_ERR_SHAPE;
   if (B == 0 || H == 0 || S == 0) return MHA_OK;
   if (!out || !dout || !lse || !dk || !dv || !delta) return MHA_ERR_NULL;
   if (!aligned(out, 16) || !aligned(dout, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
@@ -203,9 +204,18 @@ int mha_backward(const void* q, const void* k, const void* v, const void* out, c
   p.dtype = dtype;
   p.c_log2 = (float)(1.4426950408889634074 / sqrt((double)d_h));
   p.tile_cfg = tile_config();
+  p.group = (int)(H / H_kv);
   const hipError_t e = mha::launch_bwd(p, (hipStream_t)stream);
   if (e == hipErrorInvalidConfiguration) return MHA_ERR_SHAPE;
   return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
+}
+
+int mha_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t B,
+                 int64_t H, int64_t S, int64_t d_h, int causal, const int32_t* key_len, int dtype,
+                 void* stream) {
+  return mha_backward_grouped(q, k, v, out, dout, lse, dq, dk, dv, delta, B, H, H > 0 ? H : 1, S,
+                              d_h, causal, key_len, dtype, stream);
 }
 
 int mha_select_variant(int64_t B, int64_t H, int64_t S, int64_t d_h, int causal, int dtype) {
@@ -240,6 +250,6 @@ const char* mha_status_string(int status) {
   return "unknown status";
 }
 
-int mha_version(void) { return 102; }
+int mha_version(void) { return 103; }
 
 }  // extern "C"

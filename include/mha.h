@@ -165,6 +165,22 @@ int mha_backward(const void* q, const void* k, const void* v, const void* out, c
                  int64_t H, int64_t S, int64_t d_h, int causal, const int32_t* key_len, int dtype,
                  void* stream);
 
+/*
+ * mha_backward_grouped -- mha_backward for grouped-query attention: q, out,
+ * dout, dq are contiguous [B, H, S, d_h]; k, v, dk, dv are contiguous
+ * [B, H_kv, S, d_h] (H_kv >= 1 dividing H; query head h uses key / value
+ * head h / (H / H_kv), as in mha_forward_strided). The key / value
+ * gradients are summed over the query heads of each group inside one
+ * workgroup per key block, without atomics (rustingstudio
+ * "brain/docs/baseline", "Fused attention": blocking the key-side kernel on
+ * the key / value head). Other arguments and behaviour as mha_backward;
+ * MHA_ERR_SHAPE if H_kv does not divide H.
+ */
+int mha_backward_grouped(const void* q, const void* k, const void* v, const void* out,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         float* delta, int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t d_h,
+                         int causal, const int32_t* key_len, int dtype, void* stream);
+
 /* The variant mha_forward would launch for these arguments (host-only, no
  * GPU call), or a negative mha_status code if the arguments are invalid. */
 int mha_select_variant(int64_t B, int64_t H, int64_t S, int64_t d_h, int causal, int dtype);
@@ -176,7 +192,7 @@ const char* mha_variant_name(int variant);
 const char* mha_status_string(int status);
 
 /* Library ABI version (major * 100 + minor); 101 adds mha_backward, 102
- * mha_forward_strided. */
+ * mha_forward_strided, 103 mha_backward_grouped. */
 int mha_version(void);
 
 #ifdef __cplusplus

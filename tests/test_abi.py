@@ -149,3 +149,12 @@ def test_strided_validation_codes(mha):
     bad = list(s); bad[8] = 1 << 27            # one head spans >= 2^31 bytes
     assert _strided(lib, bad) == 2
     assert _strided(lib, B=0) == 0
+
+
+def test_grouped_backward_validation(mha):
+    lib = mha.load()
+    args = [0x1000 * i for i in range(1, 11)]
+    assert lib.mha_backward_grouped(*args, 1, 4, 3, 16, 64, 0, None, 1, None) == 2  # 3 !| 4
+    assert lib.mha_backward_grouped(*args, 1, 4, 0, 16, 64, 0, None, 1, None) == 2
+    assert lib.mha_backward_grouped(*args, 1, 4, 2, 16, 64, 0, None, 0, None) == 3  # fp32
+    assert lib.mha_backward_grouped(*args, 0, 4, 2, 16, 64, 0, None, 1, None) == 0  # empty

@@ -137,3 +137,35 @@ def test_backward_row_term_workspace(mha, dt):
         ref = (do.double().numpy() * o64).sum(-1)
     got = delta.cpu().double().numpy()
     assert np.allclose(got, ref, rtol=1e-4, atol=1e-4), np.abs(got - ref).max()
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(2, 8, 2, 200, 64, [200, 77]), (1, 12, 4, 1024, 64, None),
+                                   (1, 6, 1, 130, 128, [100]), (2, 4, 2, 64, 16, None)],
+                         ids=lambda s: "x".join(map(str, s[:5])))
+def test_backward_grouped_heads(mha, shape, causal, dt):
+    """Grouped-query attention: the key / value gradients of a group, summed
+    over its query heads, against the oracle's gradients of the repeated
+    heads summed over each group (the chain rule through the repetition)."""
+    B, H, Hk, S, D, key_len = shape
+    g = torch.Generator().manual_seed(H * 100 + Hk)
+    q = torch.randn(B, H, S, D, generator=g).to(DT[dt])
+    k = torch.randn(B, Hk, S, D, generator=g).to(DT[dt])
+    v = torch.randn(B, Hk, S, D, generator=g).to(DT[dt])
+    do = torch.randn(B, H, S, D, generator=g).to(DT[dt])
+    kl = None if key_len is None else torch.tensor(key_len, dtype=torch.int32)
+    dq, dk, dv = _run(mha, q, k, v, do, kl, causal)
+    grp = H // Hk
+    ke, ve = (t.repeat_interleave(grp, dim=1) for t in (k, v))
+    rq, rk, rv = oracle.attention_backward(q, ke, ve, do, causal=causal, key_len=kl,
+                                           threads=THREADS)
+    rk = rk.reshape(B, Hk, grp, S, D).sum(axis=2)
+    rv = rv.reshape(B, Hk, grp, S, D).sum(axis=2)
+    for name, u, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        ok = oracle.gate(u, r)
+        assert ok.all(), (f"{shape} {dt} causal={causal} {name}: {int((~ok).sum())} fail, "
+                          f"budget {oracle.budget_fraction(u, r):.3f}")
+    print(f"grouped {shape} causal={causal} {dt}: budget dq {oracle.budget_fraction(dq, rq):.3f} "
+          f"dk {oracle.budget_fraction(dk, rk):.3f} dv {oracle.budget_fraction(dv, rv):.3f}",
+          flush=True)

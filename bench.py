@@ -35,12 +35,12 @@ PEAK_MFMA_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}  # dense matrix
 MALL_BYTES = 256 << 20           # working sets below this are rotated over buffer sets
 
 DEFAULT_STEPS = {"tiny": 2000, "launch": 2000, "bandwidth": 100, "compute": 200, "long": 4,
-                 "bwd": 50}
-DEFAULT_WARMUP = {"tiny": 50, "launch": 50, "bandwidth": 5, "compute": 10, "long": 1, "bwd": 5}
+                 "bwd": 50, "bwd_gqa": 50}
+DEFAULT_WARMUP = {"tiny": 50, "launch": 50, "bandwidth": 5, "compute": 10, "long": 1, "bwd": 5, "bwd_gqa": 5}
 WARMUP_S = 0.5                   # minimum warm-up time before any timed region
-DEFAULT_GRAPH = {"tiny": 100, "launch": 100, "bandwidth": 0, "compute": 0, "long": 0, "bwd": 0}
+DEFAULT_GRAPH = {"tiny": 100, "launch": 100, "bandwidth": 0, "compute": 0, "long": 0, "bwd": 0, "bwd_gqa": 0}
 BOUND = {"tiny": "hbm", "launch": "hbm", "bandwidth": "hbm", "compute": "mfma", "long": "mfma",
-         "bwd": "mfma"}
+         "bwd": "mfma", "bwd_gqa": "mfma"}
 KERNEL_SOURCES = ("attn_common.h", "attn_mfma.hip", "attn_short.hip", "attn_short16.hip",
                   "attn_f32.hip", "attn_valu.hip", "launch.h", "mha_api.hip")
 
@@ -160,7 +160,7 @@ def bench_backward(args, w, mha):
     pairs = pair_count(w, kl_cpu)
     flops = 10 * w.D * pairs
     out, lse = mha.forward(q, k, v, causal=w.causal, key_len=kl)
-    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty_like(lse)
     stream = torch.cuda.current_stream(dev)
 
@@ -198,7 +198,8 @@ def bench_backward(args, w, mha):
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": tag, "data": "synthetic",
-        "config": {"workload": w.name, "pass": "backward", "B": w.B, "H": w.H, "S": w.S,
+        "config": {"workload": w.name, "pass": "backward", "B": w.B, "H": w.H,
+                   "H_kv": w.H_kv or w.H, "S": w.S,
                    "d_h": w.D, "causal": w.causal,
                    "key_len": (None if w.key_len is None else list(w.key_len)), "seed": args.seed,
                    "kernels": "row-term pass (bf16 only), dq, dk/dv", "parallelism": "single GPU"},
@@ -221,6 +222,8 @@ def bench_backward(args, w, mha):
         except Exception:
             blas = 1
         qc, kc, vc, dc = (t.cpu() for t in (q, k, v, dout))
+        if w.H_kv and w.H_kv != w.H:  # the oracle's heads: key / value heads repeated per group
+            kc, vc = (t.repeat_interleave(w.H // w.H_kv, dim=1) for t in (kc, vc))
         reps = 0
         t0 = time.perf_counter()
         while True:  # the whole workload, repeated until about 12 s have passed
@@ -255,7 +258,7 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default=None,
-                    choices=["tiny", "launch", "bandwidth", "compute", "long", "bwd"],
+                    choices=["tiny", "launch", "bandwidth", "compute", "long", "bwd", "bwd_gqa"],
                     help="default: launch for the forward, bwd for the backward")
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
                     help="time the forward (default) or the backward (dq, dk, dv)")

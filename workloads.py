@@ -43,6 +43,7 @@ class Workload:
     # ("uniform", lo, hi) -> per batch uniform on [lo, hi] inclusive.
     key_len: Optional[tuple]
     note: str = ""
+    H_kv: Optional[int] = None  # key / value heads (grouped-query attention); None = H
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -68,6 +69,10 @@ WORKLOADS = {
     # 12 heads of 64, causal, bf16 (one key/value head per query head here)
     "bwd": Workload("bwd", 4, 12, 1024, 64, torch.bfloat16, True, None,
                     "backward: B=4, S=1024, 12 heads of 64, causal, bf16"),
+    # the same with the page's 4 key / value heads (grouped-query attention)
+    "bwd_gqa": Workload("bwd_gqa", 4, 12, 1024, 64, torch.bfloat16, True, None,
+                        "backward: B=4, S=1024, 12 query / 4 key-value heads of 64, causal, bf16",
+                        H_kv=4),
 }
 
 
@@ -108,14 +113,15 @@ def make_inputs(w: Workload, seed: int, device="cpu", gen_device: Optional[str] 
 
 
 def make_backward_inputs(w: Workload, seed: int, device="cpu"):
-    """(q, k, v, key_len, dout): make_inputs, then the output gradient dout
-    drawn next from the same CPU generator, N(0, 1) in float32, cast to the
-    workload dtype."""
+    """(q, k, v, key_len, dout): q, k, v (k and v with H_kv heads when set),
+    key lengths, then the output gradient dout, drawn in that order from one
+    CPU generator, N(0, 1) in float32, cast to the workload dtype."""
     gen = torch.Generator(device="cpu")
     gen.manual_seed(int(seed))
     shape = (w.B, w.H, w.S, w.D)
-    qkv = [torch.randn(shape, generator=gen, dtype=torch.float32).to(w.dtype).to(device)
-           for _ in range(3)]
+    kv_shape = (w.B, w.H_kv or w.H, w.S, w.D)
+    qkv = [torch.randn(shp, generator=gen, dtype=torch.float32).to(w.dtype).to(device)
+           for shp in (shape, kv_shape, kv_shape)]
     kl = _draw_key_len(w, gen, device)
     dout = torch.randn(shape, generator=gen, dtype=torch.float32).to(w.dtype).to(device)
     return qkv[0], qkv[1], qkv[2], kl, dout

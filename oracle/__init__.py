@@ -13,6 +13,8 @@ Contents:
                    rule on materialised matrices (rustingstudio
                    "brain/docs/baseline", "Fused attention", describes the
                    fused kernels they check).
+  qkv.py        -- attention fed by its own QKV projection X W_qkv + b
+                   (devpost "gpu-transformer-optimization", section 2.2).
   gate.py       -- the graded elementwise accuracy rule (devpost
                    "optimized-gpu-kernels-for-transformer-layers",
                    Inspiration; devpost "transformerkernel ... Tesla T4",
@@ -22,6 +24,7 @@ Contents:
 from .attention import attention, attention_rows, valid_mask, count_valid_pairs
 from .backward import attention_backward
 from .gate import gate, budget_fraction
+from .qkv import qkv_attention, qkv_project
 
 __all__ = [
     "attention",
@@ -29,6 +32,8 @@ __all__ = [
     "valid_mask",
     "count_valid_pairs",
     "attention_backward",
+    "qkv_attention",
+    "qkv_project",
     "gate",
     "budget_fraction",
 ]

@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Attention forward benchmark on one MI355X.
 
-    python bench.py [--workload launch|bandwidth|compute|long|tiny]
-                    [--steps K] [--warmup W] [--gpus 1] [--graph G]
+    python bench.py [--workload launch|bandwidth|compute|long|tiny|qkv_launch|qkv_bandwidth]
+                    [--pass fwd|bwd] [--steps K] [--warmup W] [--gpus 1] [--graph G]
 
 One step is one exact attention forward (one launch of the library's kernel)
 over a batch of seeded synthetic inputs already resident in device memory.
@@ -35,14 +35,20 @@ PEAK_MFMA_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}  # dense matrix
 MALL_BYTES = 256 << 20           # working sets below this are rotated over buffer sets
 
 DEFAULT_STEPS = {"tiny": 2000, "launch": 2000, "bandwidth": 100, "compute": 200, "long": 4,
-                 "bwd": 50, "bwd_gqa": 50}
-DEFAULT_WARMUP = {"tiny": 50, "launch": 50, "bandwidth": 5, "compute": 10, "long": 1, "bwd": 5, "bwd_gqa": 5}
+                 "bwd": 50, "bwd_gqa": 50, "qkv_launch": 2000, "qkv_bandwidth": 100}
+DEFAULT_WARMUP = {"tiny": 50, "launch": 50, "bandwidth": 5, "compute": 10, "long": 1, "bwd": 5,
+                  "bwd_gqa": 5, "qkv_launch": 50, "qkv_bandwidth": 5}
 WARMUP_S = 0.5                   # minimum warm-up time before any timed region
-DEFAULT_GRAPH = {"tiny": 100, "launch": 100, "bandwidth": 0, "compute": 0, "long": 0, "bwd": 0, "bwd_gqa": 0}
+DEFAULT_GRAPH = {"tiny": 100, "launch": 100, "bandwidth": 0, "compute": 0, "long": 0, "bwd": 0,
+                 "bwd_gqa": 0, "qkv_launch": 100, "qkv_bandwidth": 0}
 BOUND = {"tiny": "hbm", "launch": "hbm", "bandwidth": "hbm", "compute": "mfma", "long": "mfma",
          "bwd": "mfma", "bwd_gqa": "mfma"}
+# the sources each timed path's kernels are built from (their hash marks
+# stored counter runs as current or stale)
 KERNEL_SOURCES = ("attn_common.h", "attn_mfma.hip", "attn_short.hip", "attn_short16.hip",
                   "attn_f32.hip", "attn_valu.hip", "launch.h", "mha_api.hip")
+QKV_SOURCES = ("attn_common.h", "attn_qkv16.hip", "launch.h", "mha_api.hip")
+BWD_SOURCES = ("attn_common.h", "attn_bwd.hip", "launch.h", "mha_api.hip")
 
 
 def dtype_tag(dt) -> str:
@@ -69,9 +75,9 @@ def algorithmic_bytes(w, kl_cpu, esize: int) -> int:
     return qo + kv + lse + kl
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(files=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "exact_attention_mha_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -209,7 +215,7 @@ def bench_backward(args, w, mha):
             "kernel_avg_us": round(k_avg_ms * 1e3, 3),
             "kernel_timing": "HIP events around the timed region / %d backward calls "
                              "(all kernels of a call)" % K,
-            "algorithmic_flops": flops, "kernel_source_hash": kernel_source_hash(),
+            "algorithmic_flops": flops, "kernel_source_hash": kernel_source_hash(BWD_SOURCES),
         },
         "flops_per_step": flops, "visible_pairs": pairs,
     }
@@ -240,6 +246,162 @@ def bench_backward(args, w, mha):
     return res
 
 
+def bench_qkv(args, w, mha):
+    """One step = one mha_qkv_attention call: the QKV projection of x
+    [B, S, d_model] and attention on its head slices, inputs resident in
+    device memory. FLOPs: 6 S d_model^2 per batch element for the projection
+    (x W_qkv over every row, as the definition states it) plus 4 d_h per
+    visible pair for attention. Algorithmic bytes: x, W_qkv, b_qkv and the
+    key lengths read once, out and lse written once."""
+    import torch
+    import oracle
+    from workloads import make_qkv_inputs
+
+    K = args.steps if args.steps is not None else DEFAULT_STEPS[w.name]
+    W = args.warmup if args.warmup is not None else DEFAULT_WARMUP[w.name]
+    dev = torch.device("cuda:0")
+    tag = dtype_tag(w.dtype)
+    esize = torch.tensor([], dtype=w.dtype).element_size()
+    x, wq, bq, kl = make_qkv_inputs(w, args.seed, device=dev)
+    kl_cpu = None if kl is None else kl.cpu()
+    D = w.H * w.D
+    pairs = pair_count(w, kl_cpu)
+    flops = 6 * w.B * w.S * D * D + 4 * w.D * pairs
+    nbytes = (2 * w.B * w.S * D + 3 * D * D + 3 * D) * esize + 4 * w.B * w.H * w.S \
+        + (0 if kl is None else 4 * w.B)
+    nsets = 1 if nbytes >= MALL_BYTES else max(3, min(8, math.ceil(2 * MALL_BYTES / max(nbytes, 1))))
+    xs = [x] + [x.clone() for _ in range(nsets - 1)]
+    outs = [(torch.empty_like(x), torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev))
+            for _ in range(nsets)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, s=None):
+        o, l = outs[i % nsets]
+        mha.qkv_attention(xs[i % nsets], wq, bq, n_heads=w.H, causal=w.causal, key_len=kl,
+                          out=o, lse=l, stream=stream if s is None else s)
+
+    t_w = time.perf_counter()
+    i = 0
+    while i < W or time.perf_counter() - t_w < WARMUP_S:
+        step(i)
+        i += 1
+        torch.cuda.synchronize()
+
+    def timed(run, n, st):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(st)
+        run()
+        e1.record(st)
+        torch.cuda.synchronize()
+        wall_s = time.perf_counter() - t0
+        ev = e0.elapsed_time(e1)
+        return max(ev, wall_s * 1e3) / n, ev
+
+    G = args.graph if args.graph is not None else DEFAULT_GRAPH[w.name]
+    graph = None
+    if G > 0:
+        K = max(G, (K + G - 1) // G * G)
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream(dev)
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for i in range(G):
+                    step(i, cap)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        for _ in range(max(1, W // G)):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    eager_ms, eager_ev = timed(lambda: [step(i) for i in range(K)], K, stream)
+    ms_per_step, k_ev = eager_ms, eager_ev
+    timing = "HIP events around the timed region / %d launches" % K
+    if graph is not None:
+        ms_per_step, k_ev = timed(lambda: [graph.replay() for _ in range(K // G)], K, stream)
+        timing = "HIP events around the timed graph replays / %d launches" % K
+    k_avg_ms = k_ev / K
+
+    # context: the same computation unfused -- a library GEMM for the
+    # projection (torch addmm) and the attention kernel on the head views
+    y = torch.empty((w.B, w.S, 3 * D), dtype=w.dtype, device=dev)
+    uo = torch.empty((w.B, w.S, w.H, w.D), dtype=w.dtype, device=dev).transpose(1, 2)
+    ul = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+
+    def unfused():
+        torch.addmm(bq, x.view(-1, D), wq, out=y.view(-1, 3 * D))
+        q, k, v = (t.view(w.B, w.S, w.H, w.D).transpose(1, 2) for t in y.split(D, dim=-1))
+        mha.forward(q, k, v, causal=w.causal, key_len=kl, out=uo, lse=ul, stream=stream)
+
+    for _ in range(3):
+        unfused()
+    n_u = max(1, min(K, 50))
+    unfused_ms, _ = timed(lambda: [unfused() for _ in range(n_u)], n_u, stream)
+
+    achieved = nbytes / (k_avg_ms * 1e-3) / 1e9
+    mfma_achieved = flops / (k_avg_ms * 1e-3) / 1e12
+    src_hash = kernel_source_hash(QKV_SOURCES)
+    res = {
+        "metric": "fused QKV projection + attention TFLOP/s (6 S d_model^2 projection flops per "
+                  "batch element + 4 d_h per visible pair) and % of MI355X HBM roofline",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 4),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": tag, "data": "synthetic",
+        "config": {"workload": w.name, "pass": "qkv projection + forward", "B": w.B, "S": w.S,
+                   "d_model": D, "H": w.H, "d_h": w.D, "causal": w.causal,
+                   "key_len": (None if w.key_len is None else list(w.key_len)),
+                   "seed": args.seed, "bias": True, "buffer_sets": nsets,
+                   "parallelism": "single GPU",
+                   "submission": f"hip graph of {G} calls" if graph is not None else "eager"},
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 3), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 5),
+            "traffic": stored_traffic(w.name, src_hash),
+            "kernel_avg_us": round(k_avg_ms * 1e3, 3), "kernel_timing": timing,
+            "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+            "mfma_tflops": round(mfma_achieved, 3),
+            "mfma_frac": round(mfma_achieved / PEAK_MFMA_TFLOPS[tag], 5),
+            "kernel_source_hash": src_hash,
+        },
+        "flops_per_step": flops, "visible_pairs": pairs,
+        "eager_ms_per_step": round(eager_ms, 6),
+        "unfused_ms_per_step": round(unfused_ms, 6),
+        "unfused": "torch addmm (library GEMM) + mha_forward_strided on the head views, eager",
+    }
+    if not args.no_cpu_baseline:
+        avail = len(os.sched_getaffinity(0))
+        threads = max(1, min(16, avail))
+        try:
+            from threadpoolctl import threadpool_info
+            blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        except Exception:
+            blas = 1
+        xc, wc, bc = x.cpu(), wq.cpu(), bq.cpu()
+        # batch elements in chunks of 64 (in order, wrapping) until ~12 s
+        chunk = min(64, w.B)
+        done, t0, j = 0, time.perf_counter(), 0
+        while True:
+            idx = [(j + i) % w.B for i in range(chunk)]
+            oracle.qkv_attention(xc[idx], wc, bc, w.H, causal=w.causal,
+                                 key_len=None if kl_cpu is None else kl_cpu[idx], threads=threads)
+            done += chunk
+            j += chunk
+            dt = time.perf_counter() - t0
+            if dt > 12.0:
+                break
+        frac = done / w.B
+        res["cpu_baseline"] = {"value": flops * frac / dt / 1e12, "unit": "TFLOP/s",
+                               "cores": max(blas, threads), "kind": "oracle",
+                               "sample": f"{done} batch elements (of {w.B}) in chunks of {chunk}",
+                               "seconds": round(dt, 3), "host_cores_available": avail}
+    return res
+
+
 def copy_calibration(nbytes: int, reps: int):
     """A plain device copy of known size, for scaling the HBM byte counters."""
     import torch
@@ -258,7 +420,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default=None,
-                    choices=["tiny", "launch", "bandwidth", "compute", "long", "bwd", "bwd_gqa"],
+                    choices=["tiny", "launch", "bandwidth", "compute", "long", "bwd", "bwd_gqa",
+                             "qkv_launch", "qkv_bandwidth"],
                     help="default: launch for the forward, bwd for the backward")
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
                     help="time the forward (default) or the backward (dq, dk, dv)")
@@ -293,6 +456,9 @@ def main():
     w = WORKLOADS[args.workload]
     if args.which == "bwd":
         print(json.dumps(bench_backward(args, w, mha)), flush=True)
+        return
+    if w.name.startswith("qkv_"):
+        print(json.dumps(bench_qkv(args, w, mha)), flush=True)
         return
     K = args.steps if args.steps is not None else DEFAULT_STEPS[w.name]
     W = args.warmup if args.warmup is not None else DEFAULT_WARMUP[w.name]

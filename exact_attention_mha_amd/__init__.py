@@ -9,7 +9,9 @@ library is not built, or the tensors are not on a GPU, calls raise.
 
 q, k, v: contiguous [B, H, S, d_h] tensors on the GPU (float32, float16 or
 bfloat16), d_h in {16, 32, 64, 128, 256}; key_len: None or an int32 GPU
-tensor [B] of right-padded key lengths.
+tensor [B] of right-padded key lengths. backward() gives dq, dk, dv;
+qkv_attention() takes the activations and the QKV projection weights
+instead of q, k, v, for short sequences of 16-wide heads.
 """
 
 from __future__ import annotations
@@ -19,8 +21,8 @@ import os
 from typing import Optional, Tuple
 
 __all__ = [
-    "forward", "load", "library_path", "library_built", "select_variant",
-    "VARIANTS", "DTYPES", "MhaError",
+    "forward", "backward", "qkv_attention", "load", "library_path", "library_built",
+    "select_variant", "VARIANTS", "DTYPES", "MhaError",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -74,6 +76,8 @@ def load() -> ctypes.CDLL:
     lib.mha_backward.restype = ctypes.c_int
     lib.mha_backward_grouped.argtypes = [vp] * 10 + [i64] * 5 + [ctypes.c_int, vp, ctypes.c_int, vp]
     lib.mha_backward_grouped.restype = ctypes.c_int
+    lib.mha_qkv_attention.argtypes = [vp] * 5 + [i64] * 4 + [ctypes.c_int, vp, ctypes.c_int, vp]
+    lib.mha_qkv_attention.restype = ctypes.c_int
     lib.mha_select_variant.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
     lib.mha_select_variant.restype = ctypes.c_int
     lib.mha_variant_name.argtypes = [ctypes.c_int]
@@ -242,3 +246,58 @@ def backward(q, k, v, out, lse, dout, causal: bool = False, key_len=None,
     if status != 0:
         raise MhaError("mha_backward_grouped", status, lib.mha_status_string(status).decode())
     return tuple(grads)
+
+
+def qkv_attention(x, w_qkv, b_qkv=None, n_heads: int = 8, causal: bool = False, key_len=None,
+                  out=None, lse=None, return_lse: bool = True, stream=None):
+    """Attention of the head slices of x @ w_qkv + b_qkv, projected on chip.
+
+    Args:
+      x: contiguous [B, S, d_model] GPU tensor (float16 or bfloat16), S <= 128.
+      w_qkv: contiguous [d_model, 3 d_model] (columns q | k | v), dtype of x.
+      b_qkv: None or contiguous [3 d_model], dtype of x.
+      n_heads: H, with d_model = 16 H and H in {2, 4, 8}.
+      causal, key_len: as in forward().
+      out: optional preallocated contiguous [B, S, d_model] output.
+      lse: optional preallocated float32 [B, H, S].
+    Returns:
+      (out, lse) -- out[b, :, 16h:16h+16] is head h's attention output.
+    """
+    import torch
+
+    lib = load()
+    if x.dim() != 3:
+        raise ValueError(f"x must be [B, S, d_model], got {tuple(x.shape)}")
+    B, S, D = x.shape
+    H = int(n_heads)
+    if w_qkv.shape != (D, 3 * D) or (b_qkv is not None and b_qkv.shape != (3 * D,)):
+        raise ValueError(f"w_qkv must be [{D}, {3 * D}] and b_qkv [{3 * D}]")
+    for name, t in (("x", x), ("w_qkv", w_qkv), ("b_qkv", b_qkv)):
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != x.dtype:
+            raise ValueError(f"{name} must be a contiguous GPU tensor of the dtype of x")
+    dcode = _dtype_code(x)
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype or not out.is_cuda or not out.is_contiguous():
+        raise ValueError("out must be a contiguous GPU tensor shaped and typed like x")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=x.device)
+    if lse is not None and (lse.shape != (B, H, S) or lse.dtype != torch.float32
+                            or not lse.is_contiguous() or not lse.is_cuda):
+        raise ValueError("lse must be a contiguous float32 GPU tensor [B, H, S]")
+    kl_ptr = None
+    if key_len is not None:
+        if (key_len.dtype != torch.int32 or key_len.shape != (B,) or not key_len.is_cuda
+                or not key_len.is_contiguous()):
+            raise ValueError("key_len must be a contiguous int32 GPU tensor [B]")
+        kl_ptr = key_len.data_ptr()
+    st = stream if stream is not None else torch.cuda.current_stream(x.device)
+    status = lib.mha_qkv_attention(
+        x.data_ptr(), w_qkv.data_ptr(), b_qkv.data_ptr() if b_qkv is not None else None,
+        out.data_ptr(), lse.data_ptr() if lse is not None else None,
+        B, S, D, H, int(bool(causal)), kl_ptr, dcode, st.cuda_stream)
+    if status != 0:
+        raise MhaError("mha_qkv_attention", status, lib.mha_status_string(status).decode())
+    return out, lse

@@ -124,6 +124,23 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBufferWord3 = 0x00020000;  // raw (untyped) buffer, gfx9 family
 constexpr int kOutOfRange = 0x7ffffff0;   // an offset past every range used here
 
+// 16-byte LDS read at byte address addr + OFF through inline asm, for the
+// same reason as lds_read_tr16_asm (no compiler wait for buffer->LDS copies
+// into other stages); the caller orders the result with lgkm_wait1<N>.
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read_b128_asm(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+// s_waitcnt lgkmcnt(N) tied to one value (see lgkm_wait).
+template <int N, typename V>
+__device__ __forceinline__ void lgkm_wait1(V& a) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "i"(N));
+}
+
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)nbytes, kBufferWord3);
 }

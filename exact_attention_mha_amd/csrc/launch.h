@@ -63,6 +63,22 @@ struct BwdParams {
   int group;               // query heads per key / value head (k, v, dk, dv have H / group)
 };
 
+// Attention fed by its own QKV projection (d_h = 16, S <= 128): x [B, S, 16H],
+// w [16H, 48H] (columns q | k | v, head h at 16h within each), bias [48H] or
+// null, out [B, S, 16H], lse [B, H, S] or null; all contiguous.
+struct QkvParams {
+  const void* x;
+  const void* w;
+  const void* bias;        // nullable
+  void* out;
+  float* lse;              // nullable
+  const int32_t* key_len;  // nullable
+  int B, S, H;
+  int causal;
+  int dtype;
+  float c_log2;            // log2(e) / sqrt(16)
+};
+
 hipError_t launch_bwd(const BwdParams& p, hipStream_t s);          // dq then dk/dv kernel
 
 hipError_t launch_mfma(const AttnParams& p, hipStream_t s);        // general tiled
@@ -71,5 +87,6 @@ hipError_t launch_f32(const AttnParams& p, hipStream_t s);         // fp32 input
 hipError_t launch_valu_d16(const AttnParams& p, hipStream_t s);    // d_h = 16 VALU
 hipError_t launch_short(const AttnParams& p, hipStream_t s);       // S <= 128 one pass, d_h 32/64
 hipError_t launch_short16(const AttnParams& p, hipStream_t s);     // S <= 128 one pass, d_h 16
+hipError_t launch_qkv16(const QkvParams& p, hipStream_t s);        // projection + attention, d_h 16
 
 }  // namespace mha

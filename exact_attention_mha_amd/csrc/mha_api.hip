@@ -218,6 +218,37 @@ int mha_backward(const void* q, const void* k, const void* v, const void* out, c
                               d_h, causal, key_len, dtype, stream);
 }
 
+int mha_qkv_attention(const void* x, const void* w_qkv, const void* b_qkv, void* out, float* lse,
+                      int64_t B, int64_t S, int64_t d_model, int64_t H, int causal,
+                      const int32_t* key_len, int dtype, void* stream) {
+  if (B < 0 || S < 0 || d_model <= 0 || H <= 0 || d_model % H) return MHA_ERR_SHAPE;
+  if (dtype != MHA_F16 && dtype != MHA_BF16) return MHA_ERR_UNSUPPORTED;
+  if (d_model != 16 * H || (H != 2 && H != 4 && H != 8) || S > 128) return MHA_ERR_UNSUPPORTED;
+  if (B == 0 || S == 0) return MHA_OK;
+  if (!x || !w_qkv || !out) return MHA_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(w_qkv, 2) || (b_qkv && !aligned(b_qkv, 2)))
+    return MHA_ERR_MISALIGNED;
+  if ((lse && !aligned(lse, 4)) || (key_len && !aligned(key_len, 4))) return MHA_ERR_MISALIGNED;
+  if (B * H >= ((int64_t)1 << 31)) return MHA_ERR_SHAPE;
+
+  mha::QkvParams p;
+  p.x = x;
+  p.w = w_qkv;
+  p.bias = b_qkv;
+  p.out = out;
+  p.lse = lse;
+  p.key_len = key_len;
+  p.B = (int)B;
+  p.S = (int)S;
+  p.H = (int)H;
+  p.causal = causal ? 1 : 0;
+  p.dtype = dtype;
+  p.c_log2 = (float)(1.4426950408889634074 / 4.0);  // 1 / sqrt(16)
+  const hipError_t e = mha::launch_qkv16(p, (hipStream_t)stream);
+  if (e == hipErrorInvalidConfiguration) return MHA_ERR_SHAPE;
+  return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
+}
+
 int mha_select_variant(int64_t B, int64_t H, int64_t S, int64_t d_h, int causal, int dtype) {
   (void)causal;
   if (B < 0 || H < 0 || S < 0 || d_h <= 0) return -MHA_ERR_SHAPE;
@@ -250,6 +281,6 @@ const char* mha_status_string(int status) {
   return "unknown status";
 }
 
-int mha_version(void) { return 103; }
+int mha_version(void) { return 104; }
 
 }  // extern "C"

@@ -181,6 +181,38 @@ int mha_backward_grouped(const void* q, const void* k, const void* v, const void
                          float* delta, int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t d_h,
                          int causal, const int32_t* key_len, int dtype, void* stream);
 
+/*
+ * mha_qkv_attention -- attention fed by its own QKV projection, for short
+ * sequences of 16-wide heads (devpost "gpu-transformer-optimization",
+ * section 2.2: the fused QKV projection, and the fused QKV-attention program
+ * used for S <= 128):
+ *     [Q | K | V] = x W_qkv + b_qkv,   x [B, S, d_model], W_qkv [d_model, 3 d_model]
+ *     head h of Q, K, V = columns 16h .. 16h + 15 of the respective d_model block
+ *     out[b, :, 16h .. 16h + 15] = softmax(Q_h K_h^T / 4 + mask) V_h
+ * with the mask, lse and no-visible-key conventions of mha_forward
+ * (key_len[b] clamps to [0, S]). q, k, v exist only on chip: the only
+ * device-memory traffic is x, W_qkv, b_qkv in and out, lse out.
+ *
+ *   x      contiguous [B, S, d_model], dtype; 16-byte aligned
+ *   w_qkv  contiguous [d_model, 3 d_model], dtype (columns q | k | v); 2-byte aligned
+ *   b_qkv  contiguous [3 d_model] in dtype, or NULL for no bias; 2-byte aligned
+ *   out    contiguous [B, S, d_model], dtype; 16-byte aligned (may not alias x)
+ *   lse    float [B, H, S] (natural log), or NULL; 4-byte aligned
+ *   key_len  NULL or int32 [B] in device memory
+ *   dtype  MHA_F16 or MHA_BF16
+ *
+ * Supported: d_model = 16 H with H in {2, 4, 8}, 0 <= S <= 128; otherwise
+ * MHA_ERR_UNSUPPORTED (longer sequences or other head sizes take a separate
+ * projection and mha_forward_strided). Precision: the projection
+ * accumulates in fp32; fp16 rounds q, k, v to fp16 before the attention
+ * products, bf16 carries each as a pair of bf16 values (head and
+ * remainder); attention as mha_forward. B == 0 or S == 0 launches nothing.
+ * Ownership, asynchrony and error behaviour as for mha_forward.
+ */
+int mha_qkv_attention(const void* x, const void* w_qkv, const void* b_qkv, void* out, float* lse,
+                      int64_t B, int64_t S, int64_t d_model, int64_t H, int causal,
+                      const int32_t* key_len, int dtype, void* stream);
+
 /* The variant mha_forward would launch for these arguments (host-only, no
  * GPU call), or a negative mha_status code if the arguments are invalid. */
 int mha_select_variant(int64_t B, int64_t H, int64_t S, int64_t d_h, int causal, int dtype);
@@ -192,7 +224,7 @@ const char* mha_variant_name(int variant);
 const char* mha_status_string(int status);
 
 /* Library ABI version (major * 100 + minor); 101 adds mha_backward, 102
- * mha_forward_strided, 103 mha_backward_grouped. */
+ * mha_forward_strided, 103 mha_backward_grouped, 104 mha_qkv_attention. */
 int mha_version(void);
 
 #ifdef __cplusplus

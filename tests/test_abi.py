@@ -158,3 +158,26 @@ def test_grouped_backward_validation(mha):
     assert lib.mha_backward_grouped(*args, 1, 4, 0, 16, 64, 0, None, 1, None) == 2
     assert lib.mha_backward_grouped(*args, 1, 4, 2, 16, 64, 0, None, 0, None) == 3  # fp32
     assert lib.mha_backward_grouped(*args, 0, 4, 2, 16, 64, 0, None, 1, None) == 0  # empty
+
+
+def _qkv(lib, x=0x1000, w=0x2000, b=None, out=0x4000, lse=None, B=2, S=128, D=128, H=8,
+         causal=1, key_len=None, dtype=1):
+    return lib.mha_qkv_attention(x, w, b, out, lse, B, S, D, H, causal, key_len, dtype, None)
+
+
+def test_qkv_attention_validation(mha):
+    lib = mha.load()
+    assert lib.mha_version() >= 104
+    assert _qkv(lib, x=None) == 1 and _qkv(lib, w=None) == 1 and _qkv(lib, out=None) == 1
+    assert _qkv(lib, B=-1) == 2 and _qkv(lib, S=-1) == 2 and _qkv(lib, H=0) == 2
+    assert _qkv(lib, D=100, H=8) == 2             # H does not divide d_model
+    assert _qkv(lib, D=256, H=8) == 3             # d_h = 32: not this kernel
+    assert _qkv(lib, D=256, H=16) == 3            # 16 heads
+    assert _qkv(lib, D=96, H=6) == 3
+    assert _qkv(lib, S=129) == 3                  # longer sequences: unfused path
+    assert _qkv(lib, dtype=0) == 3 and _qkv(lib, dtype=9) == 3
+    assert _qkv(lib, x=0x1008) == 4 and _qkv(lib, out=0x4004) == 4
+    assert _qkv(lib, w=0x2001) == 4 and _qkv(lib, b=0x3001) == 4
+    assert _qkv(lib, lse=0x5002) == 4 and _qkv(lib, key_len=0x6001) == 4
+    assert _qkv(lib, B=0) == 0 and _qkv(lib, S=0) == 0  # empty: nothing launched
+    assert _qkv(lib, B=0, x=None) == 0

@@ -1,0 +1,137 @@
+"""GPU parity of mha_qkv_attention (attention fed by its own QKV projection,
+d_h = 16, S <= 128) against the float64 oracle of the projection followed by
+attention, under the graded rule |u-r| <= 2e-3 or |u-r| <= 2e-2 |r|, on the
+same rounded inputs."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import THREADS
+from workloads import WORKLOADS, make_qkv_inputs
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _inputs(B, S, H, dt, seed, key_len="random", bias=True):
+    w = WORKLOADS["qkv_bandwidth"].with_(B=B, S=S, H=H, dtype=DT[dt],
+                                         key_len=("uniform", 0, S) if key_len == "random"
+                                         else key_len)
+    x, wq, bq, kl = make_qkv_inputs(w, seed)
+    return x, wq, (bq if bias else None), kl
+
+
+def _run(mha, x, wq, bq, kl, H, causal):
+    dev = [None if t is None else t.cuda() for t in (x, wq, bq, kl)]
+    out, lse = mha.qkv_attention(dev[0], dev[1], dev[2], n_heads=H, causal=causal, key_len=dev[3])
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+def _check(out, lse, x, wq, bq, kl, H, causal, label, batches=None):
+    if batches is not None:  # a sample of batch elements, computed one by one
+        x, out, lse = x[batches], out[batches], lse[batches]
+        kl = None if kl is None else kl[batches]
+    ro, rl = oracle.qkv_attention(x, wq, bq, H, causal=causal, key_len=kl, threads=THREADS)
+    ok_o, ok_l = oracle.gate(out, ro), oracle.gate(lse, rl)
+    fo, fl = oracle.budget_fraction(out, ro), oracle.budget_fraction(lse, rl)
+    if not (ok_o.all() and ok_l.all()):
+        raise AssertionError(f"{label}: {int((~ok_o).sum())} out / {int((~ok_l).sum())} lse "
+                             f"elements fail (budget out {fo:.3f}, lse {fl:.3f}); first bad "
+                             f"{np.argwhere(~ok_o)[:5].tolist()}")
+    print(f"{label}: budget out {fo:.3f} lse {fl:.3f}", flush=True)
+    return fo, fl
+
+
+CASES = [  # B, S, H
+    (3, 128, 8),
+    (2, 100, 8),   # ragged last tile
+    (5, 17, 4),
+    (4, 1, 2),
+    (1, 64, 8),
+    (700, 128, 8),  # more elements than workgroups: several per workgroup
+    (1100, 77, 4),
+]
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
+def test_qkv_attention_shapes(mha, case, causal, dt):
+    B, S, H = case
+    x, wq, bq, kl = _inputs(B, S, H, dt, seed=B + S + H)
+    out, lse = _run(mha, x, wq, bq, kl, H, causal)
+    _check(out, lse, x, wq, bq, kl, H, causal, f"qkv {case} causal={causal} {dt}")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_qkv_attention_no_bias_no_key_len(mha, dt):
+    x, wq, _, _ = _inputs(6, 128, 8, dt, seed=1, key_len=None, bias=False)
+    out, lse = _run(mha, x, wq, None, None, 8, True)
+    _check(out, lse, x, wq, None, None, 8, True, f"no bias, all keys {dt}")
+
+
+@pytest.mark.parametrize("name", ["qkv_launch", "qkv_bandwidth"])
+def test_qkv_attention_workloads(mha, name):
+    """The benchmark workloads at full size; the bandwidth one on a sample of
+    300 batch elements (every element of those) plus every key length."""
+    w = WORKLOADS[name]
+    x, wq, bq, kl = make_qkv_inputs(w, seed=0)
+    out, lse = _run(mha, x, wq, bq, kl, w.H, w.causal)
+    batches = None
+    if w.B > 300:
+        rng = np.random.default_rng(0)
+        batches = np.unique(np.concatenate([[0, w.B - 1], rng.choice(w.B, 298, replace=False)]))
+    _check(out, lse, x, wq, bq, kl, w.H, w.causal, name, batches=batches)
+
+
+def test_qkv_attention_edges(mha):
+    # no visible key in some elements: out 0, lse -inf
+    x, wq, bq, _ = _inputs(4, 40, 4, "f16", seed=3)
+    kl = torch.tensor([0, 40, 0, 7], dtype=torch.int32)
+    out, lse = _run(mha, x, wq, bq, kl, 4, True)
+    assert not out[0].any() and not out[2].any()
+    assert torch.isneginf(lse[0]).all() and torch.isneginf(lse[2]).all()
+    _check(out, lse, x, wq, bq, kl, 4, True, "key_len 0")
+    # key lengths past S clamp to S, negative to 0
+    kl = torch.tensor([-3, 500, 40, 1], dtype=torch.int32)
+    out, lse = _run(mha, x, wq, bq, kl, 4, False)
+    _check(out, lse, x, wq, bq, kl.clamp(0, 40), 4, False, "clamped key_len")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_qkv_attention_hidden_rows_stay_local(mha, dt):
+    """NaN in activation rows at or past the key length reaches only those
+    rows' own outputs: the other rows are bitwise unchanged."""
+    x, wq, bq, _ = _inputs(3, 128, 8, dt, seed=4)
+    kl = torch.tensor([50, 128, 1], dtype=torch.int32)
+    base_o, base_l = _run(mha, x, wq, bq, kl, 8, False)
+    xp = x.clone()
+    xp[0, 50:] = float("nan")
+    xp[2, 1:] = float("nan")
+    po, pl = _run(mha, xp, wq, bq, kl, 8, False)
+    assert torch.equal(po[0, :50], base_o[0, :50]) and torch.equal(pl[0, :, :50], base_l[0, :, :50])
+    assert torch.equal(po[1], base_o[1]) and torch.equal(po[2, :1], base_o[2, :1])
+    assert torch.isnan(po[0, 50:]).all()
+    _check(base_o, base_l, x, wq, bq, kl, 8, False, f"hidden rows {dt}")
+
+
+def test_qkv_attention_deterministic_and_matches_unfused(mha):
+    """Repeat calls give the same bits; the fused fp16 result agrees with the
+    library's own unfused path (projection rounded to fp16, then forward on
+    the head slices) to within one fp16 rounding of the output."""
+    x, wq, bq, kl = _inputs(64, 128, 8, "f16", seed=5)
+    a = _run(mha, x, wq, bq, kl, 8, True)
+    b = _run(mha, x, wq, bq, kl, 8, True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    xd, wd, bd, kd = (t.cuda() for t in (x, wq, bq, kl))
+    y = (xd.float() @ wd.float() + bd.float()).half()  # [B, S, 3D]
+    q, k, v = (t.reshape(64, 128, 8, 16).transpose(1, 2) for t in y.split(128, dim=-1))
+    out = torch.empty(64, 128, 8, 16, dtype=torch.float16, device="cuda").transpose(1, 2)
+    mha.forward(q, k, v, causal=True, key_len=kd, out=out)
+    torch.cuda.synchronize()
+    ref = out.transpose(1, 2).reshape(64, 128, 128).cpu().float()
+    assert (a[0].float() - ref).abs().max() <= 2e-3

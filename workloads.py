@@ -26,7 +26,8 @@ from typing import Optional, Tuple
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_backward_inputs", "sample_rows"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_backward_inputs", "make_qkv_inputs",
+           "sample_rows"]
 
 
 @dataclass(frozen=True)
@@ -64,6 +65,16 @@ WORKLOADS = {
                         "MFMA-bound: d_model=1024 in 4 heads of 256"),
     "long": Workload("long", 32, 16, 100000, 64, torch.float16, True, ("fixed", 100000),
                      "long sequence: d_model=1024 in 16 heads of 64, S=100000"),
+    # attention fed by its own QKV projection (devpost
+    # "gpu-transformer-optimization", section 2.2): the launch- and HBM-bound
+    # shapes above with x [B, S, d_model = H d_h] and W_qkv [d_model, 3 d_model]
+    # in place of q, k, v
+    "qkv_launch": Workload("qkv_launch", 1, 8, 128, 16, torch.float16, True, ("fixed", 128),
+                           "fused QKV projection + attention: B=1, S=128, d_model=128, 8 heads"),
+    "qkv_bandwidth": Workload("qkv_bandwidth", 10000, 8, 128, 16, torch.float16, True,
+                              ("uniform", 64, 128),
+                              "fused QKV projection + attention: B=10000, S=128, d_model=128, "
+                              "8 heads, right-padded key lengths"),
     # the training shape of the fused backward on rustingstudio
     # "brain/docs/baseline" ("Fused attention"): batch 4, sequence 1024,
     # 12 heads of 64, causal, bf16 (one key/value head per query head here)
@@ -125,6 +136,24 @@ def make_backward_inputs(w: Workload, seed: int, device="cpu"):
     kl = _draw_key_len(w, gen, device)
     dout = torch.randn(shape, generator=gen, dtype=torch.float32).to(w.dtype).to(device)
     return qkv[0], qkv[1], qkv[2], kl, dout
+
+
+def make_qkv_inputs(w: Workload, seed: int, device="cpu"):
+    """(x, w_qkv, b_qkv, key_len) for the fused projection workloads: x
+    [B, S, d_model] N(0, 1) (layer-normalised activations), then W_qkv
+    [d_model, 3 d_model] and b_qkv [3 d_model] uniform on +-1/sqrt(d_model)
+    (the default initialisation of a torch linear layer, the pages' randomly
+    initialised weights), then the key lengths; float32 draws from one CPU
+    generator, cast to the workload dtype."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(int(seed))
+    D = w.H * w.D
+    a = 1.0 / np.sqrt(D)
+    x = torch.randn((w.B, w.S, D), generator=gen, dtype=torch.float32)
+    wq = (torch.rand((D, 3 * D), generator=gen, dtype=torch.float32) * 2 - 1) * a
+    bq = (torch.rand((3 * D,), generator=gen, dtype=torch.float32) * 2 - 1) * a
+    kl = _draw_key_len(w, gen, device)
+    return (x.to(w.dtype).to(device), wq.to(w.dtype).to(device), bq.to(w.dtype).to(device), kl)
 
 
 def sample_rows(B: int, H: int, S: int, n_rows: int, seed: int, tile: int = 128,

@@ -66,7 +66,9 @@ enum mha_variant {
   MHA_VARIANT_VALU_D16 = 4,   /* fp16/bf16 d_h = 16 on the vector ALUs       */
   MHA_VARIANT_SHORT = 5,      /* fp16/bf16 d_h <= 64, S <= 128: one pass per
                                  head, no rescaling                          */
-  MHA_VARIANT_COUNT = 6
+  MHA_VARIANT_MFMA32 = 6,     /* fp16/bf16 d_h 64 / 128 / 256 general tiled
+                                 kernel on 32x32 matrix tiles                */
+  MHA_VARIANT_COUNT = 7
 };
 
 /*

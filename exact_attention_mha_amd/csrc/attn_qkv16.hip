@@ -282,6 +282,9 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
           s[kt] = mfma_k16(kf[kt], qh[t], init);
         }
         if (kt == kL) {  // wave-uniform
+          // (a real branch: the empty volatile statement keeps the compiler
+          // from turning this into an add and a select on every tile)
+          asm volatile("");
 #pragma unroll
           for (int i = 0; i < 4; ++i) s[kt][i] += mL[i];
         }

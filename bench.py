@@ -211,7 +211,8 @@ def bench_backward(args, w, mha):
                    "kernels": "row-term pass (bf16 only), dq, dk/dv", "parallelism": "single GPU"},
         "roofline": {
             "bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 5), "traffic": None,
+            "frac": round(achieved / peak, 5),
+            "traffic": stored_traffic(w.name, kernel_source_hash(BWD_SOURCES)),
             "kernel_avg_us": round(k_avg_ms * 1e3, 3),
             "kernel_timing": "HIP events around the timed region / %d backward calls "
                              "(all kernels of a call)" % K,

@@ -67,14 +67,18 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   constexpr int NI = (SLOTS + 63) / 64;  // DMA instructions per tile
   constexpr int TILE = NI * 64 * 8;      // elements per tile (whole DMA instructions)
   constexpr int NIW = (NI + NW - 1) / NW;
-  constexpr int NDT = D / 16;            // output column tiles
+  // output column tiles; d_h = 8 runs as one 16-wide tile whose columns
+  // 8..15 are zero (the LDS pad slot of each row holds zeros there, Q loads
+  // and O stores of those columns are out of range)
+  constexpr int NDT = D >= 16 ? D / 16 : 1;
+  constexpr bool kHalf = D == 8;
   constexpr int NKT = BK / 16;           // key tiles per block
   constexpr int NKP = BK / 32;           // key pairs per block
   constexpr int NKC = D >= 32 ? D / 32 : 1;
   constexpr int ES = (int)sizeof(T);
   constexpr int BQ = NW * NQT * 16;
   constexpr bool kBf16 = __is_same(T, bf16_t);
-  static_assert(BK % 32 == 0 && D % 16 == 0, "tile shape");
+  static_assert(BK % 32 == 0 && (D % 16 == 0 || D == 8), "tile shape");
 
   __shared__ __attribute__((aligned(16))) T smem[NST * 2 * TILE];  // [stage][K, V]
 
@@ -116,7 +120,8 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
       for (int t = 0; t < NQT; ++t) {
         const int row = wq0 + 16 * t + c;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) buf_store8(zero_vec<T4>(), ro, row * RO + (16 * dt + 4 * g) * 2);
+        for (int dt = 0; dt < NDT; ++dt)
+          buf_store8(zero_vec<T4>(), ro, kHalf && g >= 2 ? kOutOfRange : row * RO + (16 * dt + 4 * g) * 2);
         if (LSEp) buf_store4(-INFINITY, rl, g == 0 ? row * 4 : kOutOfRange);
       }
     }
@@ -156,8 +161,8 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
 #pragma unroll
   for (int t = 0; t < NQT; ++t) {
     const int row = wq0 + 16 * t + c;
-    if constexpr (D == 16) {
-      qf4[t] = buf_load8<T4>(rq, row * RQ + 4 * g * 2, 0);
+    if constexpr (D <= 16) {
+      qf4[t] = buf_load8<T4>(rq, kHalf && g >= 2 ? kOutOfRange : row * RQ + 4 * g * 2, 0);
     } else {
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) qf[t][kc] = buf_load16<T8>(rq, row * RQ + (32 * kc + 8 * g) * 2, 0);
@@ -176,7 +181,7 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   // load waits inside the loop
 #pragma unroll
   for (int t = 0; t < NQT; ++t) {
-    if constexpr (D == 16) {
+    if constexpr (D <= 16) {
       asm volatile("" : "+v"(qf4[t]));
     } else {
 #pragma unroll
@@ -228,7 +233,7 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
       const int rbase = (32 * (kt >> 1) + 16 * (kt & 1)) * STR;
 #pragma unroll
       for (int t = 0; t < NQT; ++t) s[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (D == 16) {
+      if constexpr (D <= 16) {
         const T4 kf = *(const T4*)(Ks + rbase + kread16);
 #pragma unroll
         for (int t = 0; t < NQT; ++t) s[t][kt] = mfma_k16(kf, qf4[t], s[t][kt]);
@@ -352,7 +357,7 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
         T4 ov;
 #pragma unroll
         for (int i = 0; i < 4; ++i) ov[i] = to_t<T>(o[t][dt][i] * inv);
-        buf_store8(ov, ro, row * RO + (16 * dt + 4 * g) * 2);
+        buf_store8(ov, ro, kHalf && g >= 2 ? kOutOfRange : row * RO + (16 * dt + 4 * g) * 2);
       }
       if (LSEp) buf_store4((m_run[t] + fast_log2(l)) * kLn2, rl, g == 0 ? row * 4 : kOutOfRange);
     }
@@ -378,6 +383,7 @@ template <typename T>
 static hipError_t launch_general(const AttnParams& p, hipStream_t s) {
   const int cfg = p.tile_cfg;
   switch (p.D) {
+    case 8: return launch_one<T, 8, 2, 4, 64, false>(p, s);
     case 16: return launch_one<T, 16, 2, 4, 64, false>(p, s);
     case 32: return launch_one<T, 32, 2, 4, 64, false>(p, s);
     case 64:  // default: 4 waves of 64 query rows, two workgroups per CU
@@ -402,6 +408,7 @@ static hipError_t launch_general(const AttnParams& p, hipStream_t s) {
 template <typename T>
 static hipError_t launch_small(const AttnParams& p, hipStream_t s) {
   switch (p.D) {
+    case 8: return launch_one<T, 8, 1, 1, 64, false>(p, s);
     case 16: return launch_one<T, 16, 1, 1, 64, false>(p, s);
     case 32: return launch_one<T, 32, 1, 1, 64, false>(p, s);
     case 64: return launch_one<T, 64, 1, 1, 64, false>(p, s);

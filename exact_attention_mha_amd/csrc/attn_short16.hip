@@ -1,4 +1,5 @@
-// Short-sequence attention forward for d_h = 16 heads (S <= 128), fp16/bf16.
+// Short-sequence attention forward for d_h = 16 heads (S <= 128), fp16/bf16;
+// d_h = 8 heads run the same code as 16-wide heads with zero columns 8..15.
 //
 // The regime of many tiny heads (the bandwidth-bound shape: tens of thousands
 // of heads of 128 rows x 16 columns) is decided by per-head overhead, so this
@@ -30,15 +31,18 @@ namespace mha {
 // At least two waves per SIMD: with that budget (<= 256 registers per lane)
 // the compiler keeps matrix-core results in ordinary VGPRs, where the softmax
 // reads them, instead of accumulation registers that need a copy per value.
-template <typename T, int QPW, bool CAUSAL>
+template <typename T, int D, int QPW, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2)
 attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
                  T* __restrict__ Op, float* __restrict__ LSEp, const int32_t* __restrict__ key_len,
                  int BH, int H, int S, float c_log2, Layout lay) {
   constexpr bool causal = CAUSAL;
   typedef typename Vec<T>::x4 T4;
-  constexpr int D = 16;
-  constexpr int RB = D * (int)sizeof(T);  // 32 bytes per row
+  // d_h = 16, or d_h = 8 run as a 16-wide head whose columns 8..15 are zero:
+  // lane groups g = 2, 3 (those columns) load nothing and store nothing
+  static_assert(D == 16 || D == 8, "head size");
+  constexpr bool kHalf = D == 8;
+  constexpr int RB = D * (int)sizeof(T);  // bytes per row
   constexpr int NT = 8;                    // 16-row tiles in S <= 128
   constexpr int PARTS = NT / QPW;          // waves per head
   constexpr bool kBf16 = __is_same(T, bf16_t);
@@ -46,6 +50,7 @@ attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __
 
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
+  const bool gcol = !kHalf || g < 2;  // this lane group's four columns exist
   const int item = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
   const int bh = item / PARTS, part = item - bh * PARTS;
   if (bh >= BH) return;  // wave-uniform; no barriers in this kernel
@@ -79,13 +84,13 @@ attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __
   // ---- operands straight from memory (keys past L and rows past S read 0)
   T4 qf[QPW], kf[NT], vt[NT];
 #pragma unroll
-  for (int j = 0; j < QPW; ++j) qf[j] = buf_load8<T4>(rq, (16 * tile[j] + c) * RQ + 8 * g, 0);
+  for (int j = 0; j < QPW; ++j) qf[j] = buf_load8<T4>(rq, gcol ? (16 * tile[j] + c) * RQ + 8 * g : kOutOfRange, 0);
   T4 vraw[NT];
 #pragma unroll
   for (int kt = 0; kt < NT; ++kt) {
     if (kt < kt_need) {
-      kf[kt] = buf_load8<T4>(rk, (16 * kt + c) * RK + 8 * g, 0);
-      vraw[kt] = buf_load8<T4>(rv, (16 * kt + c) * RV + 8 * g, 0);
+      kf[kt] = buf_load8<T4>(rk, gcol ? (16 * kt + c) * RK + 8 * g : kOutOfRange, 0);
+      vraw[kt] = buf_load8<T4>(rv, gcol ? (16 * kt + c) * RV + 8 * g : kOutOfRange, 0);
     }
   }
   T4 ident, ones;
@@ -121,7 +126,7 @@ attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __
     if (16 * t >= S) return;  // wave-uniform
     const int row = 16 * t + c;
     if (L == 0) {  // no visible key
-      buf_store8(zero_vec<T4>(), ro, row * RO + 8 * g);
+      buf_store8(zero_vec<T4>(), ro, gcol ? row * RO + 8 * g : kOutOfRange);
       if (LSEp) buf_store4(-INFINITY, rl, g == 0 ? row * 4 : kOutOfRange);
       return;
     }
@@ -167,7 +172,7 @@ attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __
     T4 ov;
 #pragma unroll
     for (int i = 0; i < 4; ++i) ov[i] = to_t<T>(o[i] * inv);
-    buf_store8(ov, ro, row * RO + 8 * g);  // O^T lane layout: row, columns 4g..4g+3
+    buf_store8(ov, ro, gcol ? row * RO + 8 * g : kOutOfRange);  // O^T lane layout: row, columns 4g..4g+3
     if (LSEp) buf_store4((m + fast_log2(l)) * kLn2, rl, g == 0 ? row * 4 : kOutOfRange);
     __builtin_amdgcn_sched_barrier(0);  // keep query tiles from interleaving (register pressure)
   };
@@ -176,18 +181,18 @@ attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __
   }(std::make_integer_sequence<int, QPW>{});
 }
 
-template <typename T, int QPW>
+template <typename T, int D, int QPW>
 static hipError_t launch_one_short16(const AttnParams& p, hipStream_t s) {
   constexpr int PARTS = 8 / QPW;
   const int64_t waves = (int64_t)p.B * p.H * PARTS;
   const int64_t n_wg = (waves + 3) / 4;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (p.causal)
-    hipLaunchKernelGGL((attn_fwd_short16<T, QPW, true>), dim3((unsigned)n_wg), dim3(256), 0, s,
+    hipLaunchKernelGGL((attn_fwd_short16<T, D, QPW, true>), dim3((unsigned)n_wg), dim3(256), 0, s,
                        (const T*)p.q, (const T*)p.k, (const T*)p.v, (T*)p.out, p.lse, p.key_len,
                        p.B * p.H, p.H, p.S, p.c_log2, p.lay);
   else
-    hipLaunchKernelGGL((attn_fwd_short16<T, QPW, false>), dim3((unsigned)n_wg), dim3(256), 0, s,
+    hipLaunchKernelGGL((attn_fwd_short16<T, D, QPW, false>), dim3((unsigned)n_wg), dim3(256), 0, s,
                        (const T*)p.q, (const T*)p.k, (const T*)p.v, (T*)p.out, p.lse, p.key_len,
                        p.B * p.H, p.H, p.S, p.c_log2, p.lay);
   return hipGetLastError();
@@ -195,11 +200,16 @@ static hipError_t launch_one_short16(const AttnParams& p, hipStream_t s) {
 
 // Few heads (launch-bound): split each head over 4 waves (balanced tile
 // pairs); many heads: one wave per head.
-hipError_t launch_short16(const AttnParams& p, hipStream_t s) {
-  if (p.D != 16 || p.S > 128) return hipErrorInvalidValue;
+template <typename T, int D>
+static hipError_t launch_short16_t(const AttnParams& p, hipStream_t s) {
   const bool split = (int64_t)p.B * p.H < 2048;
-  if (p.dtype == 1) return split ? launch_one_short16<f16_t, 2>(p, s) : launch_one_short16<f16_t, 8>(p, s);
-  if (p.dtype == 2) return split ? launch_one_short16<bf16_t, 2>(p, s) : launch_one_short16<bf16_t, 8>(p, s);
+  return split ? launch_one_short16<T, D, 2>(p, s) : launch_one_short16<T, D, 8>(p, s);
+}
+
+hipError_t launch_short16(const AttnParams& p, hipStream_t s) {
+  if ((p.D != 16 && p.D != 8) || p.S > 128) return hipErrorInvalidValue;
+  if (p.dtype == 1) return p.D == 16 ? launch_short16_t<f16_t, 16>(p, s) : launch_short16_t<f16_t, 8>(p, s);
+  if (p.dtype == 2) return p.D == 16 ? launch_short16_t<bf16_t, 16>(p, s) : launch_short16_t<bf16_t, 8>(p, s);
   return hipErrorInvalidValue;
 }
 

@@ -12,11 +12,11 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-bool supported_d(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
+bool supported_d(int64_t d) { return d == 8 || d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
 
 // Static kernel choice by regime (dtype, d_h, sequence length, head count):
 //  * fp32 inputs                         -> fp32 matrix-core kernel
-//  * S <= 128 and d_h == 16              -> one pass per head, no LDS (any
+//  * S <= 128 and d_h <= 16              -> one pass per head, no LDS (any
 //                                           head count: few heads are split
 //                                           over four waves each)
 //  * S <= 128 and d_h <= 64, many heads  -> one pass per head, no rescaling
@@ -26,7 +26,7 @@ bool supported_d(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128 |
 int choose(int64_t B, int64_t H, int64_t S, int64_t D, int dtype) {
   if (dtype == MHA_F32) return MHA_VARIANT_F32;
   const int64_t heads = B * H;
-  if (S <= 128 && D == 16) return MHA_VARIANT_SHORT;
+  if (S <= 128 && D <= 16) return MHA_VARIANT_SHORT;
   if (S <= 128 && D <= 64 && heads >= 512) return MHA_VARIANT_SHORT;
   const int64_t wg128 = heads * ((S + 127) / 128);
   if (wg128 < 512) return MHA_VARIANT_MFMA_SMALL;
@@ -37,7 +37,7 @@ int validate(const void* q, const void* k, const void* v, void* out, const float
              int64_t B, int64_t H, int64_t S, int64_t d_h, const int32_t* key_len, int dtype) {
   if (B < 0 || H < 0 || S < 0 || d_h <= 0) return MHA_ERR_SHAPE;
   if (dtype != MHA_F32 && dtype != MHA_F16 && dtype != MHA_BF16) return MHA_ERR_UNSUPPORTED;
-  if (!supported_d(d_h)) return MHA_ERR_UNSUPPORTED;
+  if (!supported_d(d_h) || (d_h == 8 && dtype == MHA_F32)) return MHA_ERR_UNSUPPORTED;
   if (B == 0 || H == 0 || S == 0) return MHA_OK;
   if (!q || !k || !v || !out) return MHA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
@@ -109,7 +109,7 @@ int mha_forward_variant(const void* q, const void* k, const void* v, void* out, 
     case MHA_VARIANT_MFMA: e = mha::launch_mfma(p, s); break;
     case MHA_VARIANT_MFMA_SMALL: e = mha::launch_mfma_small(p, s); break;
     case MHA_VARIANT_VALU_D16: e = mha::launch_valu_d16(p, s); break;
-    case MHA_VARIANT_SHORT: e = d_h == 16 ? mha::launch_short16(p, s) : mha::launch_short(p, s); break;
+    case MHA_VARIANT_SHORT: e = d_h <= 16 ? mha::launch_short16(p, s) : mha::launch_short(p, s); break;
     case MHA_VARIANT_MFMA32: e = mha::launch_m32(p, s); break;
   }
   if (e == hipErrorInvalidConfiguration) return MHA_ERR_SHAPE;
@@ -133,7 +133,7 @@ int mha_forward_strided(const void* q, const void* k, const void* v, void* out, 
     if (((S - 1) * ss + d_h) * esize >= ((int64_t)1 << 31)) return MHA_ERR_SHAPE;
   }
   int variant = choose(B, H, S, d_h, dtype);
-  if (variant == MHA_VARIANT_SHORT && d_h != 16)  // the d_h 32/64 short kernel is contiguous only
+  if (variant == MHA_VARIANT_SHORT && d_h > 16)  // the d_h 32/64 short kernel is contiguous only
     variant = B * H * ((S + 127) / 128) < 512 ? MHA_VARIANT_MFMA_SMALL : MHA_VARIANT_MFMA;
 
   mha::AttnParams p;
@@ -178,7 +178,7 @@ int mha_backward_grouped(const void* q, const void* k, const void* v, const void
                          int causal, const int32_t* key_len, int dtype, void* stream) {
   int st = validate(q, k, v, dq, lse, B, H, S, d_h, key_len, dtype);
   if (st != MHA_OK) return st;
-  if (dtype == MHA_F32) return MHA_ERR_UNSUPPORTED;
+  if (dtype == MHA_F32 || d_h == 8) return MHA_ERR_UNSUPPORTED;
   if (H_kv <= 0 || (H > 0 && H % H_kv != 0)) return MHA_ERR_SHAPE;
   if (B == 0 || H == 0 || S == 0) return MHA_OK;
   if (!out || !dout || !lse || !dk || !dv || !delta) return MHA_ERR_NULL;
@@ -255,7 +255,7 @@ int mha_select_variant(int64_t B, int64_t H, int64_t S, int64_t d_h, int causal,
   (void)causal;
   if (B < 0 || H < 0 || S < 0 || d_h <= 0) return -MHA_ERR_SHAPE;
   if (dtype != MHA_F32 && dtype != MHA_F16 && dtype != MHA_BF16) return -MHA_ERR_UNSUPPORTED;
-  if (!supported_d(d_h)) return -MHA_ERR_UNSUPPORTED;
+  if (!supported_d(d_h) || (d_h == 8 && dtype == MHA_F32)) return -MHA_ERR_UNSUPPORTED;
   return choose(B, H, S, d_h, dtype);
 }
 

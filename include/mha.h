@@ -85,7 +85,8 @@ enum mha_variant {
  *            returning MHA_OK). One head must span fewer than 2^31 bytes
  *            (S * d_h * element size < 2^31) and the launch must fit a
  *            2^31-1 workgroup grid.
- *   d_h      head dimension: 16, 32, 64, 128 or 256.
+ *   d_h      head dimension: 16, 32, 64, 128 or 256; also 8 for fp16 / bf16
+ *            (computed as a 16-wide head with zero columns 8..15).
  *   causal   non-zero: key j visible to row i only if j <= i.
  *   key_len  device pointer to int32[B] or NULL (all S keys valid). Values
  *            are clamped to [0, S] on the device (the host never reads them).
@@ -155,7 +156,7 @@ int mha_forward_strided(const void* q, const void* k, const void* v, void* out, 
  *   delta        caller-owned float workspace [B, H, S], 4-byte aligned;
  *                overwritten with D (it stays valid after the call).
  *   B .. dtype   as for mha_forward; dtype must be MHA_F16 or MHA_BF16
- *                (fp32 inputs return MHA_ERR_UNSUPPORTED).
+ *                (fp32 inputs and d_h = 8 return MHA_ERR_UNSUPPORTED).
  *
  * Precision: products on the matrix cores with fp32 accumulation; the
  * probabilities and dS are rounded to the input dtype as matrix-core

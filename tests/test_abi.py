@@ -55,7 +55,8 @@ def test_validation_codes(mha):
     assert _fwd(lib, S=-5) == 2
     assert _fwd(lib, D=0) == 2
     assert _fwd(lib, D=48) == 3                   # MHA_ERR_UNSUPPORTED head size
-    assert _fwd(lib, D=8) == 3
+    assert _fwd(lib, D=8, dtype=0) == 3           # d_h = 8: fp16 / bf16 only
+    assert _fwd(lib, D=4) == 3
     assert _fwd(lib, dtype=7) == 3
     assert _fwd(lib, variant=99) == 3
     assert _fwd(lib, variant=4, D=64) == 3        # VALU kernel is d_h = 16 only
@@ -181,3 +182,15 @@ def test_qkv_attention_validation(mha):
     assert _qkv(lib, lse=0x5002) == 4 and _qkv(lib, key_len=0x6001) == 4
     assert _qkv(lib, B=0) == 0 and _qkv(lib, S=0) == 0  # empty: nothing launched
     assert _qkv(lib, B=0, x=None) == 0
+
+
+def test_head_size_8(mha):
+    lib = mha.load()
+    assert lib.mha_select_variant(4, 16, 128, 8, 1, 1) == mha.VARIANTS["short"]
+    assert lib.mha_select_variant(64, 16, 1000, 8, 1, 2) == mha.VARIANTS["mfma"]
+    assert lib.mha_select_variant(2, 4, 1000, 8, 1, 2) == mha.VARIANTS["mfma_small"]
+    assert lib.mha_select_variant(2, 4, 1000, 8, 1, 0) == -3  # fp32
+    assert _fwd(lib, D=8, variant=mha.VARIANTS["valu_d16"]) == 3
+    assert _fwd(lib, D=8, variant=mha.VARIANTS["mfma32"]) == 3
+    args = [0x1000 * i for i in range(1, 11)]
+    assert lib.mha_backward(*args, 1, 2, 16, 8, 0, None, 1, None) == 3  # no backward at d_h = 8

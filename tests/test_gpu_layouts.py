@@ -36,6 +36,8 @@ CASES = [  # B, S, H, H_kv, D
     (2, 130, 4, 2, 256),
     (3, 128, 8, 4, 16),    # d_h = 16, S <= 128: the short kernel
     (1, 1000, 12, 4, 64),  # grouped heads of the pages' training layer (12 query, 4 key/value)
+    (2, 128, 16, 4, 8),    # d_h = 8, S <= 128: the short kernel
+    (1, 300, 4, 2, 8),     # d_h = 8, tiled kernel
 ]
 
 

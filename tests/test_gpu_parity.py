@@ -95,13 +95,15 @@ def _variants_for(dt, D, S):
         v.append("short")
     if D == 16:
         v.append("valu_d16")
+    if D == 8:
+        v = ["auto", "mfma", "mfma_small"] + (["short"] if S <= 128 else [])
     if D >= 64:
         v.append("mfma32")
     return v
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
-@pytest.mark.parametrize("D", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("D", [8, 16, 32, 64, 128, 256])
 @pytest.mark.parametrize("S", [1, 17, 65, 128, 200])
 @pytest.mark.parametrize("causal", [False, True])
 def test_edge_shapes(mha, dt, D, S, causal):
@@ -109,6 +111,8 @@ def test_edge_shapes(mha, dt, D, S, causal):
     {S, 0, 1, S//2 + 1} (0 = a batch with no visible key), every variant that
     accepts the shape."""
     from workloads import Workload
+    if dt == "f32" and D == 8:
+        pytest.skip("d_h = 8 takes fp16 / bf16 only (the ABI test checks the error)")
     B = 4
     w = Workload("edge", B, 3, S, D, _DT[dt], causal, None)
     q, k, v, _ = make_inputs(w, seed=S * 7 + D)
@@ -229,3 +233,19 @@ def test_mfma32_variant(mha, dt, D, causal):
     q, k, v, kl = make_inputs(w, seed=D + int(causal))
     out, lse = run_gpu(mha, q, k, v, kl, causal, "mfma32")
     check_full(out, lse, q, k, v, kl, causal, f"mfma32 {dt} D={D} causal={causal}")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [(64, 16, 128, ("uniform", 1, 128)), (2, 4, 1000, ("uniform", 1, 1000)),
+                                   (1, 2, 4096, None)], ids=["short-b64-h16", "tiled-s1000", "tiled-s4096"])
+def test_head_size_8(mha, dt, shape):
+    """d_h = 8 heads (the pages' cases with sixteen heads of 8 in a
+    d_model of 128) through the short and the tiled kernels, causal, every
+    element against the oracle."""
+    from workloads import Workload
+    B, H, S, kl_spec = shape
+    w = Workload("d8", B, H, S, 8, _DT[dt], True, kl_spec)
+    q, k, v, kl = make_inputs(w, seed=S + H)
+    for variant in (["auto", "mfma_small"] if S > 128 else ["auto", "mfma"]):
+        out, lse = run_gpu(mha, q, k, v, kl, True, variant)
+        check_full(out, lse, q, k, v, kl, True, f"d8 {shape} {dt} {variant}")

@@ -35,12 +35,12 @@ PEAK_MFMA_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}  # dense matrix
 MALL_BYTES = 256 << 20           # working sets below this are rotated over buffer sets
 
 DEFAULT_STEPS = {"tiny": 2000, "launch": 2000, "bandwidth": 100, "compute": 200, "long": 4,
-                 "bwd": 50, "bwd_gqa": 50, "qkv_launch": 2000, "qkv_bandwidth": 100}
+                 "bwd": 50, "bwd_gqa": 50, "qkv_launch": 2000, "qkv_bandwidth": 100, "qkv_heads8": 100}
 DEFAULT_WARMUP = {"tiny": 50, "launch": 50, "bandwidth": 5, "compute": 10, "long": 1, "bwd": 5,
-                  "bwd_gqa": 5, "qkv_launch": 50, "qkv_bandwidth": 5}
+                  "bwd_gqa": 5, "qkv_launch": 50, "qkv_bandwidth": 5, "qkv_heads8": 5}
 WARMUP_S = 0.5                   # minimum warm-up time before any timed region
 DEFAULT_GRAPH = {"tiny": 100, "launch": 100, "bandwidth": 0, "compute": 0, "long": 0, "bwd": 0,
-                 "bwd_gqa": 0, "qkv_launch": 100, "qkv_bandwidth": 0}
+                 "bwd_gqa": 0, "qkv_launch": 100, "qkv_bandwidth": 0, "qkv_heads8": 0}
 BOUND = {"tiny": "hbm", "launch": "hbm", "bandwidth": "hbm", "compute": "mfma", "long": "mfma",
          "bwd": "mfma", "bwd_gqa": "mfma"}
 # the sources each timed path's kernels are built from (their hash marks
@@ -422,7 +422,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default=None,
                     choices=["tiny", "launch", "bandwidth", "compute", "long", "bwd", "bwd_gqa",
-                             "qkv_launch", "qkv_bandwidth"],
+                             "qkv_launch", "qkv_bandwidth", "qkv_heads8"],
                     help="default: launch for the forward, bwd for the backward")
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
                     help="time the forward (default) or the backward (dq, dk, dv)")

@@ -254,15 +254,16 @@ def qkv_attention(x, w_qkv, b_qkv=None, n_heads: int = 8, causal: bool = False, 
     """Attention of the head slices of x @ w_qkv + b_qkv, projected on chip.
 
     Args:
-      x: contiguous [B, S, d_model] GPU tensor (float16 or bfloat16), S <= 128.
+      x: contiguous [B, S, d_model] GPU tensor (float16 or bfloat16), S <= 128,
+        d_model in {32, 64, 128}.
       w_qkv: contiguous [d_model, 3 d_model] (columns q | k | v), dtype of x.
       b_qkv: None or contiguous [3 d_model], dtype of x.
-      n_heads: H, with d_model = 16 H and H in {2, 4, 8}.
+      n_heads: H, with head size d_model / H of 16 or 8.
       causal, key_len: as in forward().
       out: optional preallocated contiguous [B, S, d_model] output.
       lse: optional preallocated float32 [B, H, S].
     Returns:
-      (out, lse) -- out[b, :, 16h:16h+16] is head h's attention output.
+      (out, lse) -- out[b, :, hd h : hd (h + 1)] is head h's attention output.
     """
     import torch
 

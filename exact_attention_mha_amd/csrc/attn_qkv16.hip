@@ -1,13 +1,20 @@
-// Attention fed by its own QKV projection, for d_h = 16 heads and S <= 128
-// (fp16 / bf16): out[b] = attention of the head slices of X[b] W_qkv + b_qkv,
+// Attention fed by its own QKV projection, for d_h = 16 or 8 heads and
+// S <= 128 (fp16 / bf16): out[b] = attention of the head slices of
+// X[b] W_qkv + b_qkv,
 // with the projected q, k, v never leaving the chip (devpost
 // "gpu-transformer-optimization", section 2.2: the fused QKV-attention
 // program reads the activations once and writes only the output).
 //
-// Work decomposition. A workgroup holds one wave per head (H = d_model / 16
-// waves) and walks over batch elements (persistent grid, one or two
-// workgroups per CU). Each wave keeps its head's 48 weight columns in
-// registers for the whole run, loaded once. The [S, d_model] activation tile
+// Work decomposition. A workgroup holds one wave per 16 projection columns
+// (d_model / 16 waves: one head of 16, or two heads of 8, per wave) and
+// walks over batch elements (persistent grid, one or two workgroups per CU).
+// Each wave keeps its 48 weight columns in registers for the whole run,
+// loaded once. With heads of 8 the projection uses all 16 columns of its
+// products (the pages' heads-per-dot grouping, devpost
+// "gpu-transformer-optimization", section 2.2); each head's scores then
+// contract over its own columns only (the other head's columns of q are
+// zero), and of the 16 output columns of each head's P V product only its
+// own are kept. The [S, d_model] activation tile
 // of a batch element is copied into LDS by buffer->LDS DMA (double-buffered,
 // the next element's copy overlapping this element's attention) and read by
 // every head.
@@ -49,14 +56,15 @@
 
 namespace mha {
 
-template <typename T, int NH, bool CAUSAL>
+template <typename T, int NH, int HPW, bool CAUSAL>
 __global__ void __launch_bounds__(NH * 64, 2)
 attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restrict__ bias,
            T* __restrict__ Op, float* __restrict__ LSEp, const int32_t* __restrict__ key_len,
            int B, int S, float c_log2) {
   typedef typename Vec<T>::x4 T4;
   typedef typename Vec<T>::x8 T8;
-  constexpr int DM = 16 * NH;       // model width
+  constexpr int DM = 16 * NH;       // model width: 16 projection columns per wave
+  constexpr int NHEAD = NH * HPW;   // heads (d_h = 16 / HPW)
   constexpr int RB = 2 * DM;        // bytes per activation / output row
   constexpr int NCH = RB / 16;      // 16-byte chunks per row
   constexpr int RPL = 16 / NCH;     // rows per 256-byte LDS line
@@ -67,6 +75,7 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
   // a projected k or v tile: fp16 the rounded values, bf16 [head | remainder]
   typedef std::conditional_t<kSplit, T8, T4> KV;
   static_assert(NH == 2 || NH == 4 || NH == 8, "d_model 32, 64 or 128");
+  static_assert(HPW == 1 || HPW == 2, "one head of 16 or two heads of 8 per wave");
   static_assert(TB == 4 * NH * 1024, "four 1 KiB copies per wave fill a tile");
   __shared__ __attribute__((aligned(16))) char xs[2 * TB];
 
@@ -159,13 +168,14 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
   for (int it = 0; bb < B; ++it, bb += G) {
     const int st = it & 1;
     // This wave's copies of tile bb have landed: they were issued before the
-    // 2 * NT stores of the previous element, which may still be in flight.
+    // (1 + HPW) * NT stores of the previous element, which may still be in
+    // flight.
     // After the barrier every wave's copies have landed, and every wave is
     // done reading the other stage.
     if (it == 0)
       wait_vmem();
     else
-      wait_vmem_keep<2 * NT>();
+      wait_vmem_keep<(1 + HPW) * NT>();
     block_barrier();
     // the next element's copy overlaps all of this element's work
     if (bb + G < B) issue(bb + G, st ^ 1);
@@ -236,113 +246,144 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
     }
 
     // ---- attention per query tile --------------------------------------
-    // Every query tile issues exactly two stores (output, row lse), dropped
-    // where out of range, so each element ends with 2 * NT stores in flight.
+    // Every query tile issues exactly 1 + HPW stores (output, each head's
+    // row lse), dropped where out of range, so each element ends with
+    // (1 + HPW) * NT stores in flight.
     const rsrc_t ro = make_rsrc(Op + (int64_t)bb * S * DM, (uint32_t)(S * RB));
-    const rsrc_t rl = LSEp ? make_rsrc(LSEp + ((int64_t)bb * NH + h) * S, (uint32_t)S * 4)
-                           : make_rsrc(Op, 0u);
+    rsrc_t rl[HPW];
+#pragma unroll
+    for (int j = 0; j < HPW; ++j)
+      rl[j] = LSEp ? make_rsrc(LSEp + ((int64_t)bb * NHEAD + HPW * h + j) * S, (uint32_t)S * 4)
+                   : make_rsrc(Op, 0u);
+    // with two heads per wave, lane group g holds columns of head g / 2 (in
+    // Q, K and the output), and V column c belongs to head c / 8
+    const int gh = HPW == 2 ? g >> 1 : 0;
     auto qtile = [&](auto J) {
       constexpr int t = decltype(J)::value;
       const int row = 16 * t + c;
-      const int ooff = row * RB + 32 * h + 8 * g;  // head h's columns, lane g's four
+      const int ooff = row * RB + 32 * h + 8 * g;  // this wave's columns, lane g's four
       if (16 * t >= S || L == 0) {  // wave-uniform: no rows, or no visible key
         buf_store8(zt4, ro, 16 * t >= S ? kOutOfRange : ooff);
-        buf_store4(-INFINITY, rl, (16 * t >= S || g != 0) ? kOutOfRange : row * 4);
+#pragma unroll
+        for (int j = 0; j < HPW; ++j)
+          buf_store4(-INFINITY, rl[j], (16 * t >= S || g != 2 * j) ? kOutOfRange : row * 4);
         return;
       }
-      T8 qa, qb;  // [q | q] for the K = 32 score products (bf16: head, remainder)
-      if constexpr (kSplit) {
+      T4 q4 = zt4, l4 = zt4;  // this tile's q (bf16: head and remainder)
+      if constexpr (!kSplit) {
+        q4 = qh[t];
+      } else {
         T8 xf[NK];
         read_tile(J, st_off, xf);
         f32x4 aq = bq, ak, av;
         project(std::integral_constant<int, 0>{}, xf, true, false, aq, ak, av);
-        T4 h4, l4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          h4[i] = to_t<T>(aq[i]);
-          l4[i] = to_t<T>(aq[i] - to_f(h4[i]));
+          q4[i] = to_t<T>(aq[i]);
+          l4[i] = to_t<T>(aq[i] - to_f(q4[i]));
         }
-        qa = __builtin_shufflevector(h4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
-        qb = __builtin_shufflevector(l4, l4, 0, 1, 2, 3, 4, 5, 6, 7);
       }
       constexpr int NKT = CAUSAL ? t + 1 : NT;  // key tiles computed at most
       const int klast = min(CAUSAL ? t : NT - 1, (L - 1) >> 4);
-      f32x4 s[NT];
-      float mx = -INFINITY;
+      f32x4 o[HPW], lsum[HPW];
+      float m[HPW];
 #pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) {
-        if (kt > klast) break;
-        // the causal diagonal starts from its constant mask; the tile
-        // holding the key length then adds its offsets
-        const f32x4 init = (CAUSAL && kt == t) ? diag : zero4;
+      for (int j = 0; j < HPW; ++j) {
+        // head j's scores: the other head's columns of q are zero, so the
+        // 16-wide product contracts over head j's columns only
+        const bool mine = gh == j;
+        const T4 qm = mine ? q4 : zt4;
+        const T8 qa = __builtin_shufflevector(qm, qm, 0, 1, 2, 3, 4, 5, 6, 7);
+        T8 qb;
         if constexpr (kSplit) {
-          s[kt] = mfma_k32(kf[kt], qa, init);
-          s[kt] = mfma_k32(kf[kt], qb, s[kt]);
-        } else {
-          s[kt] = mfma_k16(kf[kt], qh[t], init);
+          const T4 lm = mine ? l4 : zt4;
+          qb = __builtin_shufflevector(lm, lm, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-        if (kt == kL) {  // wave-uniform
-          // (a real branch: the empty volatile statement keeps the compiler
-          // from turning this into an add and a select on every tile)
-          asm volatile("");
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s[kt][i] += mL[i];
-        }
-        mx = max3(mx, s[kt][0], s[kt][1]);
-        mx = max3(mx, s[kt][2], s[kt][3]);
-      }
-      const float m = group_max(mx) * c_log2;  // finite: key 0 is visible
-      auto probs = [&](const f32x4& sv, T4& hi, T4& lo) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = fast_exp2(fmaf(sv[i], c_log2, -m));
-          hi[i] = to_t<T>(pv);
-          if constexpr (kSplit) lo[i] = to_t<T>(pv - to_f(hi[i]));
-        }
-      };
-      f32x4 o = zero4, lsum = zero4;
-      if constexpr (kSplit) {
+        f32x4 sc[NT];
+        float mx = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
           if (kt > klast) break;
-          T4 ph, pl;
-          probs(s[kt], ph, pl);
-          o = mfma_k32(vt[kt], __builtin_shufflevector(ph, ph, 0, 1, 2, 3, 4, 5, 6, 7), o);
-          o = mfma_k32(vt[kt], __builtin_shufflevector(pl, pl, 0, 1, 2, 3, 4, 5, 6, 7), o);
-          lsum = mfma_k32(ones8, __builtin_shufflevector(ph, pl, 0, 1, 2, 3, 4, 5, 6, 7), lsum);
-        }
-      } else {
-        // key tiles in pairs: one K = 32 product covers keys 16k0 + 4g + e
-        // (slots e < 4) and 16k1 + 4g + e - 4 (slots e >= 4)
+          // the causal diagonal starts from its constant mask; the tile
+          // holding the key length then adds its offsets
+          const f32x4 init = (CAUSAL && kt == t) ? diag : zero4;
+          if constexpr (kSplit) {
+            sc[kt] = mfma_k32(kf[kt], qa, init);
+            sc[kt] = mfma_k32(kf[kt], qb, sc[kt]);
+          } else {
+            sc[kt] = mfma_k16(kf[kt], qm, init);
+          }
+          if (kt == kL) {  // wave-uniform
+            // (a real branch: the empty volatile statement keeps the
+            // compiler from turning this into an add and a select on every
+            // tile)
+            asm volatile("");
 #pragma unroll
-        for (int kp = 0; kp < (NKT + 1) / 2; ++kp) {
-          const int k0 = 2 * kp, k1 = 2 * kp + 1;
-          if (k0 > klast) break;
-          T4 p0, p1 = zt4, unused;
-          probs(s[k0], p0, unused);
-          if (k1 < NKT && k1 <= klast) probs(s[k1], p1, unused);
-          const T8 a = __builtin_shufflevector(vt[k0], vt[k1], 0, 1, 2, 3, 4, 5, 6, 7);
-          const T8 pb = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
-          o = mfma_k32(a, pb, o);
-          lsum = mfma_k32(ones8, pb, lsum);
+            for (int i = 0; i < 4; ++i) sc[kt][i] += mL[i];
+          }
+          mx = max3(mx, sc[kt][0], sc[kt][1]);
+          mx = max3(mx, sc[kt][2], sc[kt][3]);
+        }
+        m[j] = group_max(mx) * c_log2;  // finite: key 0 is visible
+        auto probs = [&](const f32x4& sv, T4& hi, T4& lo) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pv = fast_exp2(fmaf(sv[i], c_log2, -m[j]));
+            hi[i] = to_t<T>(pv);
+            if constexpr (kSplit) lo[i] = to_t<T>(pv - to_f(hi[i]));
+          }
+        };
+        // all 16 value columns are multiplied; only head j's columns of
+        // o[j] are kept below
+        o[j] = zero4;
+        lsum[j] = zero4;
+        if constexpr (kSplit) {
+#pragma unroll
+          for (int kt = 0; kt < NKT; ++kt) {
+            if (kt > klast) break;
+            T4 ph, pl;
+            probs(sc[kt], ph, pl);
+            o[j] = mfma_k32(vt[kt], __builtin_shufflevector(ph, ph, 0, 1, 2, 3, 4, 5, 6, 7), o[j]);
+            o[j] = mfma_k32(vt[kt], __builtin_shufflevector(pl, pl, 0, 1, 2, 3, 4, 5, 6, 7), o[j]);
+            lsum[j] = mfma_k32(ones8, __builtin_shufflevector(ph, pl, 0, 1, 2, 3, 4, 5, 6, 7), lsum[j]);
+          }
+        } else {
+          // key tiles in pairs: one K = 32 product covers keys 16k0 + 4g + e
+          // (slots e < 4) and 16k1 + 4g + e - 4 (slots e >= 4)
+#pragma unroll
+          for (int kp = 0; kp < (NKT + 1) / 2; ++kp) {
+            const int k0 = 2 * kp, k1 = 2 * kp + 1;
+            if (k0 > klast) break;
+            T4 p0, p1 = zt4, unused;
+            probs(sc[k0], p0, unused);
+            if (k1 < NKT && k1 <= klast) probs(sc[k1], p1, unused);
+            const T8 a = __builtin_shufflevector(vt[k0], vt[k1], 0, 1, 2, 3, 4, 5, 6, 7);
+            const T8 pb = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
+            o[j] = mfma_k32(a, pb, o[j]);
+            lsum[j] = mfma_k32(ones8, pb, lsum[j]);
+          }
         }
       }
-      const float l = lsum[0];  // every row of the ones product holds the full sum
-      const float inv = __builtin_amdgcn_rcpf(l);
+      // the O^T lane layout holds row `row`, columns 4g..4g+3: head gh's
+      const f32x4 os = HPW == 2 && gh == 1 ? o[HPW - 1] : o[0];
+      const float ls = HPW == 2 && gh == 1 ? lsum[HPW - 1][0] : lsum[0][0];  // every row holds the sum
+      const float inv = __builtin_amdgcn_rcpf(ls);
       T4 ov;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ov[i] = to_t<T>(o[i] * inv);
-      buf_store8(ov, ro, ooff);  // O^T lane layout: row, columns 4g..4g+3
-      buf_store4((m + fast_log2(l)) * kLn2, rl, g == 0 ? row * 4 : kOutOfRange);
+      for (int i = 0; i < 4; ++i) ov[i] = to_t<T>(os[i] * inv);
+      buf_store8(ov, ro, ooff);
+#pragma unroll
+      for (int j = 0; j < HPW; ++j)
+        buf_store4((m[j] + fast_log2(lsum[j][0])) * kLn2, rl[j], g == 2 * j ? row * 4 : kOutOfRange);
       __builtin_amdgcn_sched_barrier(0);  // keep query tiles from interleaving (register pressure)
     };
     static_for<NT>(qtile);
   }
 }
 
-template <typename T, int NH, bool C>
+template <typename T, int NH, int HPW, bool C>
 static hipError_t launch_qkv_t(const QkvParams& p, hipStream_t s) {
-  auto kern = attn_qkv16<T, NH, C>;
+  auto kern = attn_qkv16<T, NH, HPW, C>;
   // persistent grid: as many workgroups as fit on the device at once
   static int per_cu[64];
   int dev = 0;
@@ -361,17 +402,27 @@ static hipError_t launch_qkv_t(const QkvParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T, int NH>
+template <typename T, int NH, int HPW>
 static hipError_t launch_qkv_h(const QkvParams& p, hipStream_t s) {
-  return p.causal ? launch_qkv_t<T, NH, true>(p, s) : launch_qkv_t<T, NH, false>(p, s);
+  return p.causal ? launch_qkv_t<T, NH, HPW, true>(p, s) : launch_qkv_t<T, NH, HPW, false>(p, s);
 }
 
+// waves = d_model / 16; heads of 16 (one per wave) or of 8 (two per wave)
 template <typename T>
 static hipError_t launch_qkv_d(const QkvParams& p, hipStream_t s) {
-  switch (p.H) {
-    case 2: return launch_qkv_h<T, 2>(p, s);
-    case 4: return launch_qkv_h<T, 4>(p, s);
-    case 8: return launch_qkv_h<T, 8>(p, s);
+  const int waves = p.H * p.hd / 16;
+  if (p.hd == 16) {
+    switch (waves) {
+      case 2: return launch_qkv_h<T, 2, 1>(p, s);
+      case 4: return launch_qkv_h<T, 4, 1>(p, s);
+      case 8: return launch_qkv_h<T, 8, 1>(p, s);
+    }
+  } else if (p.hd == 8) {
+    switch (waves) {
+      case 2: return launch_qkv_h<T, 2, 2>(p, s);
+      case 4: return launch_qkv_h<T, 4, 2>(p, s);
+      case 8: return launch_qkv_h<T, 8, 2>(p, s);
+    }
   }
   return hipErrorInvalidValue;
 }

@@ -63,9 +63,10 @@ struct BwdParams {
   int group;               // query heads per key / value head (k, v, dk, dv have H / group)
 };
 
-// Attention fed by its own QKV projection (d_h = 16, S <= 128): x [B, S, 16H],
-// w [16H, 48H] (columns q | k | v, head h at 16h within each), bias [48H] or
-// null, out [B, S, 16H], lse [B, H, S] or null; all contiguous.
+// Attention fed by its own QKV projection (d_h = hd in {8, 16}, S <= 128):
+// x [B, S, hd H], w [hd H, 3 hd H] (columns q | k | v, head h at hd h within
+// each), bias [3 hd H] or null, out [B, S, hd H], lse [B, H, S] or null; all
+// contiguous.
 struct QkvParams {
   const void* x;
   const void* w;
@@ -73,10 +74,10 @@ struct QkvParams {
   void* out;
   float* lse;              // nullable
   const int32_t* key_len;  // nullable
-  int B, S, H;
+  int B, S, H, hd;
   int causal;
   int dtype;
-  float c_log2;            // log2(e) / sqrt(16)
+  float c_log2;            // log2(e) / sqrt(hd)
 };
 
 hipError_t launch_bwd(const BwdParams& p, hipStream_t s);          // dq then dk/dv kernel

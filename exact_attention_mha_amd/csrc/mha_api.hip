@@ -225,7 +225,9 @@ int mha_qkv_attention(const void* x, const void* w_qkv, const void* b_qkv, void*
                       const int32_t* key_len, int dtype, void* stream) {
   if (B < 0 || S < 0 || d_model <= 0 || H <= 0 || d_model % H) return MHA_ERR_SHAPE;
   if (dtype != MHA_F16 && dtype != MHA_BF16) return MHA_ERR_UNSUPPORTED;
-  if (d_model != 16 * H || (H != 2 && H != 4 && H != 8) || S > 128) return MHA_ERR_UNSUPPORTED;
+  const int64_t hd = d_model / H;
+  if ((hd != 16 && hd != 8) || (d_model != 32 && d_model != 64 && d_model != 128) || S > 128)
+    return MHA_ERR_UNSUPPORTED;
   if (B == 0 || S == 0) return MHA_OK;
   if (!x || !w_qkv || !out) return MHA_ERR_NULL;
   if (!aligned(x, 16) || !aligned(out, 16) || !aligned(w_qkv, 2) || (b_qkv && !aligned(b_qkv, 2)))
@@ -243,9 +245,10 @@ int mha_qkv_attention(const void* x, const void* w_qkv, const void* b_qkv, void*
   p.B = (int)B;
   p.S = (int)S;
   p.H = (int)H;
+  p.hd = (int)hd;
   p.causal = causal ? 1 : 0;
   p.dtype = dtype;
-  p.c_log2 = (float)(1.4426950408889634074 / 4.0);  // 1 / sqrt(16)
+  p.c_log2 = (float)(1.4426950408889634074 / sqrt((double)hd));
   const hipError_t e = mha::launch_qkv16(p, (hipStream_t)stream);
   if (e == hipErrorInvalidConfiguration) return MHA_ERR_SHAPE;
   return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
@@ -284,6 +287,6 @@ const char* mha_status_string(int status) {
   return "unknown status";
 }
 
-int mha_version(void) { return 104; }
+int mha_version(void) { return 105; }
 
 }  // extern "C"

@@ -186,15 +186,18 @@ int mha_backward_grouped(const void* q, const void* k, const void* v, const void
 
 /*
  * mha_qkv_attention -- attention fed by its own QKV projection, for short
- * sequences of 16-wide heads (devpost "gpu-transformer-optimization",
+ * sequences of 16- or 8-wide heads (devpost "gpu-transformer-optimization",
  * section 2.2: the fused QKV projection, and the fused QKV-attention program
- * used for S <= 128):
+ * used for S <= 128, with heads of 8 grouped in pairs per 16-wide product):
  *     [Q | K | V] = x W_qkv + b_qkv,   x [B, S, d_model], W_qkv [d_model, 3 d_model]
- *     head h of Q, K, V = columns 16h .. 16h + 15 of the respective d_model block
- *     out[b, :, 16h .. 16h + 15] = softmax(Q_h K_h^T / 4 + mask) V_h
+ *     head h of Q, K, V = columns hd h .. hd h + hd - 1 of the respective
+ *                         d_model block, hd = d_model / H
+ *     out[b, :, hd h .. hd h + hd - 1] = softmax(Q_h K_h^T / sqrt(hd) + mask) V_h
  * with the mask, lse and no-visible-key conventions of mha_forward
  * (key_len[b] clamps to [0, S]). q, k, v exist only on chip: the only
- * device-memory traffic is x, W_qkv, b_qkv in and out, lse out.
+ * device-memory traffic is x, W_qkv, b_qkv in and out, lse out. Activation
+ * rows at or past key_len[b] are query rows, but their keys and values are
+ * hidden: their contents (even non-finite) reach only their own outputs.
  *
  *   x      contiguous [B, S, d_model], dtype; 16-byte aligned
  *   w_qkv  contiguous [d_model, 3 d_model], dtype (columns q | k | v); 2-byte aligned
@@ -204,9 +207,10 @@ int mha_backward_grouped(const void* q, const void* k, const void* v, const void
  *   key_len  NULL or int32 [B] in device memory
  *   dtype  MHA_F16 or MHA_BF16
  *
- * Supported: d_model = 16 H with H in {2, 4, 8}, 0 <= S <= 128; otherwise
- * MHA_ERR_UNSUPPORTED (longer sequences or other head sizes take a separate
- * projection and mha_forward_strided). Precision: the projection
+ * Supported: d_model in {32, 64, 128} with hd = d_model / H in {8, 16}, and
+ * 0 <= S <= 128; otherwise MHA_ERR_UNSUPPORTED (longer sequences or other
+ * head sizes take a separate projection and mha_forward_strided);
+ * MHA_ERR_SHAPE if H does not divide d_model. Precision: the projection
  * accumulates in fp32; fp16 rounds q, k, v to fp16 before the attention
  * products, bf16 carries each as a pair of bf16 values (head and
  * remainder); attention as mha_forward. B == 0 or S == 0 launches nothing.
@@ -227,7 +231,8 @@ const char* mha_variant_name(int variant);
 const char* mha_status_string(int status);
 
 /* Library ABI version (major * 100 + minor); 101 adds mha_backward, 102
- * mha_forward_strided, 103 mha_backward_grouped, 104 mha_qkv_attention. */
+ * mha_forward_strided, 103 mha_backward_grouped, 104 mha_qkv_attention,
+ * 105 d_h = 8 (mha_forward*, mha_qkv_attention). */
 int mha_version(void);
 
 #ifdef __cplusplus

@@ -168,13 +168,16 @@ def _qkv(lib, x=0x1000, w=0x2000, b=None, out=0x4000, lse=None, B=2, S=128, D=12
 
 def test_qkv_attention_validation(mha):
     lib = mha.load()
-    assert lib.mha_version() >= 104
+    assert lib.mha_version() >= 105
     assert _qkv(lib, x=None) == 1 and _qkv(lib, w=None) == 1 and _qkv(lib, out=None) == 1
     assert _qkv(lib, B=-1) == 2 and _qkv(lib, S=-1) == 2 and _qkv(lib, H=0) == 2
     assert _qkv(lib, D=100, H=8) == 2             # H does not divide d_model
     assert _qkv(lib, D=256, H=8) == 3             # d_h = 32: not this kernel
     assert _qkv(lib, D=256, H=16) == 3            # 16 heads
     assert _qkv(lib, D=96, H=6) == 3
+    assert _qkv(lib, D=128, H=32) == 3            # d_h = 4
+    assert _qkv(lib, D=96, H=12) == 3             # d_model 96
+    assert _qkv(lib, D=128, H=16, B=0) == 0       # d_h = 8 accepted (empty: nothing launched)
     assert _qkv(lib, S=129) == 3                  # longer sequences: unfused path
     assert _qkv(lib, dtype=0) == 3 and _qkv(lib, dtype=9) == 3
     assert _qkv(lib, x=0x1008) == 4 and _qkv(lib, out=0x4004) == 4

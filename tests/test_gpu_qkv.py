@@ -16,8 +16,8 @@ pytestmark = pytest.mark.gpu
 DT = {"f16": torch.float16, "bf16": torch.bfloat16}
 
 
-def _inputs(B, S, H, dt, seed, key_len="random", bias=True):
-    w = WORKLOADS["qkv_bandwidth"].with_(B=B, S=S, H=H, dtype=DT[dt],
+def _inputs(B, S, H, dt, seed, key_len="random", bias=True, hd=16):
+    w = WORKLOADS["qkv_bandwidth"].with_(B=B, S=S, H=H, D=hd, dtype=DT[dt],
                                          key_len=("uniform", 0, S) if key_len == "random"
                                          else key_len)
     x, wq, bq, kl = make_qkv_inputs(w, seed)
@@ -135,3 +135,36 @@ def test_qkv_attention_deterministic_and_matches_unfused(mha):
     torch.cuda.synchronize()
     ref = out.transpose(1, 2).reshape(64, 128, 128).cpu().float()
     assert (a[0].float() - ref).abs().max() <= 2e-3
+
+
+CASES8 = [  # B, S, H with heads of 8 (d_model = 8 H)
+    (3, 128, 16),   # sixteen heads of 8 in d_model 128 (the pages' heads-of-8 cases)
+    (2, 100, 8),
+    (5, 17, 4),
+    (700, 128, 16),
+]
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", CASES8, ids=lambda c: "x".join(map(str, c)))
+def test_qkv_attention_heads_of_8(mha, case, causal, dt):
+    """Two heads of 8 per 16-wide projection slice: each head's scores over
+    its own columns, its own softmax, its own output columns and lse row."""
+    B, S, H = case
+    x, wq, bq, kl = _inputs(B, S, H, dt, seed=B + S + H + 1, hd=8)
+    out, lse = _run(mha, x, wq, bq, kl, H, causal)
+    _check(out, lse, x, wq, bq, kl, H, causal, f"qkv d8 {case} causal={causal} {dt}")
+
+
+def test_qkv_attention_heads_of_8_hidden_rows(mha):
+    x, wq, bq, _ = _inputs(2, 128, 16, "f16", seed=12, hd=8)
+    kl = torch.tensor([70, 3], dtype=torch.int32)
+    base_o, base_l = _run(mha, x, wq, bq, kl, 16, True)
+    xp = x.clone()
+    xp[0, 70:] = float("nan")
+    xp[1, 3:] = float("inf")
+    po, pl = _run(mha, xp, wq, bq, kl, 16, True)
+    assert torch.equal(po[0, :70], base_o[0, :70]) and torch.equal(po[1, :3], base_o[1, :3])
+    assert torch.equal(pl[0, :, :70], base_l[0, :, :70])
+    _check(base_o, base_l, x, wq, bq, kl, 16, True, "d8 hidden rows")

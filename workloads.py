@@ -75,6 +75,12 @@ WORKLOADS = {
                               ("uniform", 64, 128),
                               "fused QKV projection + attention: B=10000, S=128, d_model=128, "
                               "8 heads, right-padded key lengths"),
+    # the same with sixteen heads of 8 in d_model 128 (the pages' heads-of-8
+    # cases, grouped two per 16-wide projection slice)
+    "qkv_heads8": Workload("qkv_heads8", 10000, 16, 128, 8, torch.float16, True,
+                           ("uniform", 64, 128),
+                           "fused QKV projection + attention: B=10000, S=128, d_model=128, "
+                           "16 heads of 8, right-padded key lengths"),
     # the training shape of the fused backward on rustingstudio
     # "brain/docs/baseline" ("Fused attention"): batch 4, sequence 1024,
     # 12 heads of 64, causal, bf16 (one key/value head per query head here)

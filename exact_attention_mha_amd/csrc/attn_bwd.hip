@@ -96,12 +96,20 @@ struct BwdTile {
 // MODE kRowRead: dQ with D read from the workspace.
 constexpr int kRowFromOut = 0, kRowPass = 1, kRowRead = 2;
 
+// The kernel bodies take their block index, the number of blocks of their
+// kind and their LDS, so that one launch can run both kinds (below).
+template <typename T, int D, int BK, int NW>
+struct DqLds {
+  static constexpr int BYTES = 2 * 2 * BwdTile<T, D, BK, NW>::ELEMS * (int)sizeof(T);
+};
+
 template <typename T, int D, int NQT, int NW, int BK, int MODE>
-__global__ void __launch_bounds__(NW * 64, 2)
-attn_bwd_dq(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
-            const T* __restrict__ Op, const T* __restrict__ dOp, const float* __restrict__ LSEp,
-            T* __restrict__ dQp, float* __restrict__ Dp, const int32_t* __restrict__ key_len,
-            int H, int S, int causal, int n_qblk, float c_log2, float scale, int group) {
+__device__ __forceinline__ void bwd_dq_body(
+    uint32_t blk, uint32_t nblk_grid, T* __restrict__ smem, const T* __restrict__ Qp,
+    const T* __restrict__ Kp, const T* __restrict__ Vp, const T* __restrict__ Op,
+    const T* __restrict__ dOp, const float* __restrict__ LSEp, T* __restrict__ dQp,
+    float* __restrict__ Dp, const int32_t* __restrict__ key_len, int H, int S, int causal,
+    int n_qblk, float c_log2, float scale, int group) {
   typedef typename Vec<T>::x8 T8;
   typedef typename Vec<T>::x4 T4;
   typedef BwdTile<T, D, BK, NW> Tile;
@@ -115,13 +123,13 @@ attn_bwd_dq(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restr
   constexpr bool kBf16 = __is_same(T, bf16_t);
   static_assert(BK % 32 == 0 && D % 16 == 0, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) T smem[2 * 2 * Tile::ELEMS];  // [stage][K, V]
+  // smem: [stage][K, V] tiles
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
 
-  const uint32_t logical = xcd_logical_id(blockIdx.x, gridDim.x);
+  const uint32_t logical = xcd_logical_id(blk, nblk_grid);
   const uint32_t bh = logical / (uint32_t)n_qblk;
   int qb = (int)(logical - bh * (uint32_t)n_qblk);
   if (causal) qb = n_qblk - 1 - qb;  // heaviest causal tiles first
@@ -332,12 +340,19 @@ attn_bwd_dq(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restr
 }
 
 // --------------------------------------------------------------- dkv kernel
+template <typename T, int D, int BQb, int NW>
+struct DkvLds {
+  static constexpr int TILE_BYTES = 2 * 2 * BwdTile<T, D, BQb, NW>::ELEMS * (int)sizeof(T);
+  static constexpr int BYTES = TILE_BYTES + 2 * 2 * 64 * 4;  // + [stage][lse, D] rows
+};
+
 template <typename T, int D, int NKTW, int NW, int BQb>
-__global__ void __launch_bounds__(NW * 64, 2)
-attn_bwd_dkv(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
-             const T* __restrict__ dOp, const float* __restrict__ LSEp, const float* __restrict__ Dp,
-             T* __restrict__ dKp, T* __restrict__ dVp, const int32_t* __restrict__ key_len,
-             int H, int S, int causal, int n_kblk, float c_log2, float scale, int group) {
+__device__ __forceinline__ void bwd_dkv_body(
+    uint32_t blk, uint32_t nblk_grid, T* __restrict__ smem, float* __restrict__ svec,
+    const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
+    const T* __restrict__ dOp, const float* __restrict__ LSEp, const float* __restrict__ Dp,
+    T* __restrict__ dKp, T* __restrict__ dVp, const int32_t* __restrict__ key_len, int H, int S,
+    int causal, int n_kblk, float c_log2, float scale, int group) {
   typedef typename Vec<T>::x8 T8;
   typedef typename Vec<T>::x4 T4;
   typedef BwdTile<T, D, BQb, NW> Tile;
@@ -351,9 +366,7 @@ attn_bwd_dkv(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __rest
   constexpr int ROWF = 64;             // floats in one row-vector stage (one DMA instruction)
   static_assert(BQb % 32 == 0 && BQb <= ROWF && D % 16 == 0, "tile shape");
 
-  // [stage][Q, dO][lse, D]
-  __shared__ __attribute__((aligned(16))) T smem[2 * 2 * Tile::ELEMS];
-  __shared__ __attribute__((aligned(16))) float svec[2 * 2 * ROWF];
+  // smem: [stage][Q, dO] tiles; svec: [stage][lse, D] rows
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -363,7 +376,7 @@ attn_bwd_dkv(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __rest
   // query blocks of every query head of the group, so the key / value
   // gradients of grouped-query attention are complete without atomics
   const int Hk = H / group;
-  const uint32_t logical = xcd_logical_id(blockIdx.x, gridDim.x);
+  const uint32_t logical = xcd_logical_id(blk, nblk_grid);
   const uint32_t bh = logical / (uint32_t)n_kblk;  // over B * Hk
   const int kb = (int)(logical - bh * (uint32_t)n_kblk);
   const int b = (int)(bh / (uint32_t)Hk);
@@ -565,6 +578,64 @@ attn_bwd_dkv(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __rest
   }
 }
 
+// ---------------------------------------------------------------- kernels
+template <typename T, int D, int NQT, int NW, int BK, int MODE>
+__global__ void __launch_bounds__(NW * 64, 2)
+attn_bwd_dq(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
+            const T* __restrict__ Op, const T* __restrict__ dOp, const float* __restrict__ LSEp,
+            T* __restrict__ dQp, float* __restrict__ Dp, const int32_t* __restrict__ key_len,
+            int H, int S, int causal, int n_qblk, float c_log2, float scale, int group) {
+  __shared__ __attribute__((aligned(16))) char lds[DqLds<T, D, BK, NW>::BYTES];
+  bwd_dq_body<T, D, NQT, NW, BK, MODE>(blockIdx.x, gridDim.x, (T*)lds, Qp, Kp, Vp, Op, dOp, LSEp,
+                                       dQp, Dp, key_len, H, S, causal, n_qblk, c_log2, scale, group);
+}
+
+template <typename T, int D, int NKTW, int NW, int BQb>
+__global__ void __launch_bounds__(NW * 64, 2)
+attn_bwd_dkv(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
+             const T* __restrict__ dOp, const float* __restrict__ LSEp, const float* __restrict__ Dp,
+             T* __restrict__ dKp, T* __restrict__ dVp, const int32_t* __restrict__ key_len,
+             int H, int S, int causal, int n_kblk, float c_log2, float scale, int group) {
+  typedef DkvLds<T, D, BQb, NW> Lds;
+  __shared__ __attribute__((aligned(16))) char lds[Lds::BYTES];
+  bwd_dkv_body<T, D, NKTW, NW, BQb>(blockIdx.x, gridDim.x, (T*)lds, (float*)(lds + Lds::TILE_BYTES),
+                                    Qp, Kp, Vp, dOp, LSEp, Dp, dKp, dVp, key_len, H, S, causal,
+                                    n_kblk, c_log2, scale, group);
+}
+
+// Both kinds in one launch, once the row term D is in the workspace: the
+// first n_kv_pad blocks are key-side blocks (n_kv of them live; the count is
+// padded to a multiple of 8 so that both kinds keep their XCD-aware order),
+// the rest query-side blocks reading D. The two kinds share the workgroup's
+// LDS; a causal problem's heaviest blocks of each kind start first, and
+// the lighter ones of both fill the machine behind them instead of each
+// kernel ending on its own partly empty tail.
+template <typename T, int D, int NQT, int NW, int BK, int NKTW, int BQb>
+__global__ void __launch_bounds__(NW * 64, 2)
+attn_bwd_both(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
+              const T* __restrict__ dOp, const float* __restrict__ LSEp, const float* __restrict__ Dp,
+              T* __restrict__ dQp, T* __restrict__ dKp, T* __restrict__ dVp,
+              const int32_t* __restrict__ key_len, int H, int S, int causal, int n_qblk,
+              int n_kblk, uint32_t n_kv, uint32_t n_kv_pad, uint32_t n_q, float c_log2,
+              float scale, int group) {
+  typedef DkvLds<T, D, BQb, NW> KvLds;
+  constexpr int BYTES = KvLds::BYTES > DqLds<T, D, BK, NW>::BYTES ? KvLds::BYTES
+                                                                  : DqLds<T, D, BK, NW>::BYTES;
+  __shared__ __attribute__((aligned(16))) char lds[BYTES];
+  const uint32_t id = blockIdx.x;  // wave-uniform
+  if (id < n_kv_pad) {
+    if (id < n_kv)
+      bwd_dkv_body<T, D, NKTW, NW, BQb>(id, n_kv, (T*)lds, (float*)(lds + KvLds::TILE_BYTES), Qp,
+                                        Kp, Vp, dOp, LSEp, Dp, dKp, dVp, key_len, H, S, causal,
+                                        n_kblk, c_log2, scale, group);
+  } else {
+    // (the output pointer is not read in this mode: Qp stands in for it)
+    bwd_dq_body<T, D, NQT, NW, BK, kRowRead>(id - n_kv_pad, n_q, (T*)lds, Qp, Kp, Vp, Qp, dOp,
+                                             LSEp, dQp, const_cast<float*>(Dp), key_len, H, S,
+                                             causal, n_qblk, c_log2, scale, group);
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 template <typename T, int D, int NQT, int NW, int BK, int NKTW, int BQb>
 static hipError_t launch_bwd_one(const BwdParams& p, hipStream_t s) {
@@ -583,16 +654,28 @@ static hipError_t launch_bwd_one(const BwdParams& p, hipStream_t s) {
     hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;
   }
-  constexpr int kDqMode = kBf16 ? kRowRead : kRowFromOut;
-  hipLaunchKernelGGL((attn_bwd_dq<T, D, NQT, NW, BK, kDqMode>), dim3((unsigned)wq), dim3(NW * 64), 0, s,
-                     (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.out, (const T*)p.dout,
-                     p.lse, (T*)p.dq, p.delta, p.key_len, p.H, p.S, p.causal, n_qblk, p.c_log2, scale, p.group);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dkv<T, D, NKTW, NW, BQb>), dim3((unsigned)wk), dim3(NW * 64), 0, s,
-                     (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.dout, p.lse, p.delta,
-                     (T*)p.dk, (T*)p.dv, p.key_len, p.H, p.S, p.causal, n_kblk, p.c_log2, scale, p.group);
-  return hipGetLastError();
+  if constexpr (kBf16) {
+    // dQ and dK / dV in one launch behind the row pass
+    const int64_t wk_pad = (wk + 7) / 8 * 8;
+    if (wk_pad + wq > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((attn_bwd_both<T, D, NQT, NW, BK, NKTW, BQb>), dim3((unsigned)(wk_pad + wq)),
+                       dim3(NW * 64), 0, s, (const T*)p.q, (const T*)p.k, (const T*)p.v,
+                       (const T*)p.dout, p.lse, p.delta, (T*)p.dq, (T*)p.dk, (T*)p.dv, p.key_len,
+                       p.H, p.S, p.causal, n_qblk, n_kblk, (uint32_t)wk, (uint32_t)wk_pad,
+                       (uint32_t)wq, p.c_log2, scale, p.group);
+    return hipGetLastError();
+  } else {
+    // fp16: the dq kernel writes D (from dout and out) for the key side
+    hipLaunchKernelGGL((attn_bwd_dq<T, D, NQT, NW, BK, kRowFromOut>), dim3((unsigned)wq), dim3(NW * 64), 0, s,
+                       (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.out, (const T*)p.dout,
+                       p.lse, (T*)p.dq, p.delta, p.key_len, p.H, p.S, p.causal, n_qblk, p.c_log2, scale, p.group);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dkv<T, D, NKTW, NW, BQb>), dim3((unsigned)wk), dim3(NW * 64), 0, s,
+                       (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.dout, p.lse, p.delta,
+                       (T*)p.dk, (T*)p.dv, p.key_len, p.H, p.S, p.causal, n_kblk, p.c_log2, scale, p.group);
+    return hipGetLastError();
+  }
 }
 
 template <typename T>

@@ -186,22 +186,19 @@ __device__ __forceinline__ void wait_vmem_keep() {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// max(a, b, c). Its operands are often fresh matrix-core results, and a
-// vector-ALU read of one needs wait states after the producing instruction
-// that only the compiler inserts (it does not look inside inline asm), so
-// this stays plain code; the compiler still forms one v_max3_f32 per call,
-// plus a quieting move at the head of a chain.
-__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
-
-// max(a, b) as one v_max_f32, without the quieting moves the compiler puts
-// around fmaxf. Only for operands produced by ordinary vector-ALU
-// instructions (the lane permutes below), never straight from a matrix-core
-// result. Operands are never NaN here (masked scores are -inf).
-__device__ __forceinline__ float max2(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
+// max(a, b, c) as IEEE 754-2019 maximum (NaN-propagating): one
+// v_maximum3_f32. The fmaxf form (NaN-ignoring) needs an extra quieting
+// instruction for every operand the compiler cannot prove canonical, which
+// includes every matrix-core result. With either form a NaN score makes its
+// row NaN (its exponential is NaN), as in the definition. Plain code, so
+// the compiler inserts the wait states a read of a fresh matrix-core result
+// needs.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
+
+// max(a, b), the same way.
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 // Workgroup barrier without the release fence of __syncthreads (which would
 // drain every outstanding global->LDS copy). Callers order their own copies

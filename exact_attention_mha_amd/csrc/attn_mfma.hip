@@ -364,6 +364,416 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   }
 }
 
+// ---------------------------------------------------------------------------
+// Software-pipelined forward (fp16 / bf16, d_h >= 32). Same tiles, LDS layout
+// and copies as attn_fwd_mfma; the loop differs in two ways.
+//
+// Probabilities of a key pair use the running max as it stands, without first
+// taking the block's own maximum: p = exp2(s c - m) only has to be checked
+// for overflow. The matrix-core row sum of the pair (ones times the rounded
+// probabilities, which the denominator needs anyway) is finite exactly when
+// no probability of the pair overflowed the input dtype or was NaN. A pair
+// that fails -- the first visible keys of a row, or a row whose maximum
+// jumped by more than the dtype's range (2^16 for fp16) -- recomputes its
+// scores, moves the running max to their maximum, rescales O and l by
+// exp2(m_old - m_new) and redoes its probabilities. Numerator and denominator
+// always share one max, so the quotient is that of the online-softmax
+// recurrence (devpost "gpu-transformer-optimization", section 2.1); rounded
+// probabilities keep their relative precision at any magnitude below the
+// dtype's maximum.
+//
+// The loop is software pipelined: the step for key pair p of block kb issues,
+// in one stretch of straight-line code,
+//     the scores of pair p of block kb+1 (into the registers that pair p of
+//     block kb releases),
+//     the products O += V P of the previous pair (pair p-1 of block kb, or
+//     the last pair of block kb-1), and
+//     the exponentials of pair p of block kb,
+// so the vector and transcendental work of the softmax has independent
+// matrix-core work beside it. K of block kb+1 and V of block kb-1 are then
+// resident with block kb, so the copies rotate over four LDS stages (block
+// kb+2 in flight). All LDS reads go through inline asm with explicit
+// lgkmcnt waits, counted over one stream of reads per step.
+template <typename T, int D, int NQT, int NW, int BK, int MINB>
+__global__ void __launch_bounds__(NW * 64, MINB)
+attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
+              T* __restrict__ Op, float* __restrict__ LSEp, const int32_t* __restrict__ key_len,
+              int H, int S, int causal, int n_qblk, float c_log2, Layout lay) {
+  typedef typename Vec<T>::x8 T8;
+  typedef typename Vec<T>::x4 T4;
+  constexpr int NST = 4;
+  constexpr int STR = D + 8;
+  constexpr int SPR = D / 8 + 1;
+  constexpr int SLOTS = BK * SPR;
+  constexpr int NI = (SLOTS + 63) / 64;
+  constexpr int TILE = NI * 64 * 8;
+  constexpr int NIW = (NI + NW - 1) / NW;
+  constexpr int NDT = D / 16;
+  constexpr int NKT = BK / 16;
+  constexpr int NKP = BK / 32;
+  constexpr int NKC = D / 32;
+  constexpr int ES = (int)sizeof(T);
+  constexpr int BQ = NW * NQT * 16;
+  constexpr bool kBf16 = __is_same(T, bf16_t);
+  constexpr uint32_t kStage = 2 * TILE * ES;  // bytes per LDS stage (K tile, V tile)
+  static_assert(BK % 32 == 0 && D % 32 == 0, "tile shape");
+  static_assert(TILE * ES < 65536, "ds_read offsets within a tile");
+
+  __shared__ __attribute__((aligned(16))) T smem[NST * 2 * TILE];  // [stage][K, V]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 15, g = lane >> 4;
+
+  const uint32_t logical = xcd_logical_id(blockIdx.x, gridDim.x);
+  const uint32_t bh = logical / (uint32_t)n_qblk;
+  int qb = (int)(logical - bh * (uint32_t)n_qblk);
+  if (causal) qb = n_qblk - 1 - qb;  // heaviest causal tiles are dispatched first
+  const int b = (int)(bh / (uint32_t)H);
+  const int h = (int)(bh - (uint32_t)b * (uint32_t)H);
+  const int L = clamp_len(key_len, b, S);
+  const T* Qh = Qp + b * lay.q_b + h * lay.q_h;
+  const T* Kh = Kp + b * lay.k_b + (h / lay.group) * lay.k_h;
+  const T* Vh = Vp + b * lay.v_b + (h / lay.group) * lay.v_h;
+  T* Oh = Op + b * lay.o_b + h * lay.o_h;
+  const int RQ = lay.q_s * ES, RK = lay.k_s * ES, RV = lay.v_s * ES, RO = lay.o_s * ES;
+  auto span = [](int n, int rs) { return (uint32_t)((n - 1) * rs + D * ES); };
+
+  const int q_start = qb * BQ;
+  const int q_end = min(S, q_start + BQ);
+  const int kend = causal ? min(L, q_end) : L;
+  const int nblk = (kend + BK - 1) / BK;
+  const int wq0 = q_start + wave * NQT * 16;
+  const bool wave_live = wq0 < S;
+  const int kend_w = !wave_live ? 0 : (causal ? min(L, min(q_end, wq0 + NQT * 16)) : L);
+  const int nblk_w = (kend_w + BK - 1) / BK;  // blocks this wave computes (wave-uniform)
+
+  const rsrc_t ro = make_rsrc(Oh, span(S, RO));
+  const rsrc_t rl = make_rsrc(LSEp + (int64_t)bh * S, (uint32_t)S * 4);
+
+  if (nblk == 0) {  // no visible key (L == 0): out = 0, lse = -inf
+    if (wave_live) {
+#pragma unroll
+      for (int t = 0; t < NQT; ++t) {
+        const int row = wq0 + 16 * t + c;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) buf_store8(zero_vec<T4>(), ro, row * RO + (16 * dt + 4 * g) * 2);
+        if (LSEp) buf_store4(-INFINITY, rl, g == 0 ? row * 4 : kOutOfRange);
+      }
+    }
+    return;
+  }
+
+  const rsrc_t rk = make_rsrc(Kh, span(kend, RK));
+  const rsrc_t rv = make_rsrc(Vh, span(kend, RV));
+  int koff[NIW], voff[NIW];
+#pragma unroll
+  for (int i = 0; i < NIW; ++i) {
+    const int slot = (wave + i * NW) * 64 + lane;
+    const int row = slot / SPR, j = slot - row * SPR;
+    const bool live = slot < SLOTS && j < D / 8;
+    const int base = 32 * (row >> 5);
+    koff[i] = live ? (base + k_key_of_row(row & 31)) * RK + 16 * j : kOutOfRange;
+    voff[i] = live ? (base + v_key_of_row(row & 31)) * RV + 16 * j : kOutOfRange;
+  }
+  auto dma_block = [&](int st, int k0) __attribute__((always_inline)) {
+    T* Kst = smem + st * 2 * TILE;
+    T* Vst = Kst + TILE;
+#pragma unroll
+    for (int i = 0; i < NIW; ++i) {
+      const int inst = wave + i * NW;
+      if (NI % NW == 0 || inst < NI) {  // wave-uniform
+        dma16(rk, Kst + inst * 512, koff[i], k0 * RK);
+        dma16(rv, Vst + inst * 512, voff[i], k0 * RV);
+      }
+    }
+  };
+
+  const rsrc_t rq = make_rsrc(Qh, span(S, RQ));
+  T8 qf[NQT][NKC];
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    const int row = wq0 + 16 * t + c;
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) qf[t][kc] = buf_load16<T8>(rq, row * RQ + (32 * kc + 8 * g) * 2, 0);
+  }
+  asm volatile("" ::: "memory");
+  dma_block(0, 0);
+  dma_block(1, BK);
+  wait_vmem_keep<2 * (NI / NW)>();  // Q and block 0 have landed
+#pragma unroll
+  for (int t = 0; t < NQT; ++t)
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) asm volatile("" : "+v"(qf[t][kc]));
+  block_barrier();
+
+  constexpr float kNoMax = -1.0e30f;  // finite: exp2(s c - kNoMax) overflows, exp2(-inf) stays 0
+  float m_run[NQT], l_run[NQT];
+  f32x4 o[NQT][NDT];
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    m_run[t] = kNoMax;
+    l_run[t] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  T8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = to_t<T>(1.f);
+  const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // LDS byte addresses of this lane's operands in stage 0
+  const uint32_t kaddr0 = lds_addr(smem + c * STR + 8 * g);
+  const uint32_t vaddr0 =
+      lds_addr(smem + TILE + (16 * (g >> 1) + 8 * (g & 1) + 2 * (c >> 2)) * STR + 4 * (c & 3));
+
+  // key k0 + 32p + 8g + 4h + i is visible to row r iff key < L and, when
+  // causal, key <= r
+  auto mask_pair = [&](int p, int k0, f32x4 (&sp)[NQT][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < NQT; ++t) {
+      const int row = wq0 + 16 * t + c;
+      const int lim = (causal ? min(L - 1, row) : L - 1) - k0 - 32 * p - 8 * g;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sp[t][hh][i] = 4 * hh + i <= lim ? sp[t][hh][i] : -INFINITY;
+    }
+  };
+  // rounded probabilities of key tile hh of one pair for query tile t
+  auto prob_unit = [&](int t, int hh, const f32x4 (&sp)[NQT][2], T8 (&pf)[NQT], T8 (&pl)[NQT])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = fast_exp2(fmaf(sp[t][hh][i], c_log2, -m_run[t]));
+      pf[t][4 * hh + i] = to_t<T>(a);
+      if constexpr (kBf16) pl[t][4 * hh + i] = to_t<T>(a - to_f(pf[t][4 * hh + i]));
+    }
+  };
+  auto probs = [&](const f32x4 (&sp)[NQT][2], T8 (&pf)[NQT], T8 (&pl)[NQT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < NQT; ++t) {
+      prob_unit(t, 0, sp, pf, pl);
+      prob_unit(t, 1, sp, pf, pl);
+    }
+  };
+  // row sum of one pair for query tile t on the matrix cores
+  auto pair_sum = [&](int t, const T8 (&pf)[NQT], const T8 (&pl)[NQT]) __attribute__((always_inline)) {
+    f32x4 a = mfma_k32(ones, pf[t], zero4);
+    if constexpr (kBf16) a = mfma_k32(ones, pl[t], a);
+    return a;
+  };
+  // true if any sum is not finite; ps takes query c's sum (every row of the
+  // product holds it)
+  auto check = [&](const f32x4 (&psv)[NQT], float (&ps)[NQT]) __attribute__((always_inline)) {
+    bool bad = false;
+#pragma unroll
+    for (int t = 0; t < NQT; ++t) {
+      ps[t] = psv[t][0];
+      bad |= !(ps[t] <= 3.0e38f);
+    }
+    return bad;
+  };
+  auto no_work = [](auto) __attribute__((always_inline)) {};
+
+  // One pipeline step's LDS stream: NVI items of V^T (two transposed reads
+  // each; products O += V P with probabilities pp, pl of key pair PV) then
+  // NKI items of K (one read each; scores of key pair PK into sp, key tile
+  // j / NKC, depth chunk j % NKC). LA items are in flight ahead of their
+  // products; LDS operations complete in issue order, so each item waits for
+  // all but the reads issued after it. work(i) runs before item i's
+  // products, and a scheduling fence closes each item, so the vector work
+  // sits between the matrix-core products instead of in one run.
+  auto stream = [&](auto PV, auto NVI_, auto PK, auto NKI_, uint32_t va_base, uint32_t ka_base,
+                    const T8 (&pp)[NQT], const T8 (&pl)[NQT], f32x4 (&sp)[NQT][2], auto&& work)
+      __attribute__((always_inline)) {
+    constexpr int pv = decltype(PV)::value, pk = decltype(PK)::value;
+    constexpr int NVI = decltype(NVI_)::value, NKI = decltype(NKI_)::value;
+    constexpr int NIT = NVI + NKI;
+    constexpr int LA = NIT < 4 ? NIT : 4;
+    i16x4 va[NVI > 0 ? NVI : 1], vb[NVI > 0 ? NVI : 1];
+    u32x4 kf[NKI > 0 ? NKI : 1];
+    auto issue = [&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i < NVI) {
+        va[i] = lds_read_tr16_asm<(32 * pv * STR + 16 * i) * ES>(va_base);
+        vb[i] = lds_read_tr16_asm<((32 * pv + 1) * STR + 16 * i) * ES>(va_base);
+      } else {
+        constexpr int j = i - NVI;
+        kf[j] = lds_read_b128_asm<((32 * pk + 16 * (j / NKC)) * STR + 32 * (j % NKC)) * ES>(ka_base);
+      }
+    };
+    static_for<LA>(issue);
+    static_for<NIT>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i + LA < NIT) issue(std::integral_constant<int, i + LA>{});
+      work(I);
+      constexpr int last = i + LA < NIT ? i + LA : NIT - 1;
+      // LDS operations issued after item i: 2 per V item, 1 per K item
+      constexpr int nv_after = (last < NVI ? last : NVI - 1) - (i < NVI ? i : NVI - 1);
+      constexpr int nk_after = (last >= NVI ? last - NVI + 1 : 0) - (i >= NVI ? i - NVI + 1 : 0);
+      constexpr int after = 2 * (nv_after > 0 ? nv_after : 0) + nk_after;
+      static_assert(after >= 0 && after < 16, "lgkmcnt range");
+      if constexpr (i < NVI) {
+        lgkm_wait<after>(va[i], vb[i]);
+        const T8 vf = __builtin_bit_cast(T8, __builtin_shufflevector(va[i], vb[i], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int t = 0; t < NQT; ++t) {
+          o[t][i] = mfma_k32(vf, pp[t], o[t][i]);
+          if constexpr (kBf16) o[t][i] = mfma_k32(vf, pl[t], o[t][i]);
+        }
+      } else {
+        constexpr int j = i - NVI;
+        lgkm_wait1<after>(kf[j]);
+        const T8 k8 = __builtin_bit_cast(T8, kf[j]);
+#pragma unroll
+        for (int t = 0; t < NQT; ++t)
+          sp[t][j / NKC] = mfma_k32(k8, qf[t][j % NKC], j % NKC == 0 ? zero4 : sp[t][j / NKC]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  auto scores_pair = [&](auto P, uint32_t ka, f32x4 (&sp)[NQT][2]) __attribute__((always_inline)) {
+    T8 dummy[NQT];
+    stream(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, P,
+           std::integral_constant<int, 2 * NKC>{}, 0u, ka, dummy, dummy, sp, no_work);
+  };
+  // a pair whose sums are not finite: recompute its scores, move the running
+  // max to their maximum, rescale O and l, and redo its probabilities. One
+  // query tile at a time, each K fragment read and waited for on its own, so
+  // this rare path adds few live registers to the loop.
+  auto redo = [&](auto P, uint32_t ka, int k0, bool edge, T8 (&pf)[NQT], T8 (&pl)[NQT], float (&ps)[NQT])
+      __attribute__((always_inline)) {
+    constexpr int p = decltype(P)::value;
+    static_for<NQT>([&](auto TT) __attribute__((always_inline)) {
+      constexpr int t = decltype(TT)::value;
+      f32x4 sr[NQT][2];  // only row t is used
+      static_for<2 * NKC>([&](auto J) __attribute__((always_inline)) {
+        constexpr int j = decltype(J)::value;
+        u32x4 kf = lds_read_b128_asm<((32 * p + 16 * (j / NKC)) * STR + 32 * (j % NKC)) * ES>(ka);
+        lgkm_wait1<0>(kf);
+        sr[t][j / NKC] = mfma_k32(__builtin_bit_cast(T8, kf), qf[t][j % NKC], j % NKC == 0 ? zero4 : sr[t][j / NKC]);
+      });
+      if (edge) {
+        const int row = wq0 + 16 * t + c;
+        const int lim = (causal ? min(L - 1, row) : L - 1) - k0 - 32 * p - 8 * g;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sr[t][hh][i] = 4 * hh + i <= lim ? sr[t][hh][i] : -INFINITY;
+      }
+      float mx = max3(sr[t][0][0], sr[t][0][1], sr[t][0][2]);
+      mx = max3(mx, sr[t][0][3], sr[t][1][0]);
+      mx = max3(mx, sr[t][1][1], sr[t][1][2]);
+      mx = max2(mx, sr[t][1][3]);
+      const float m_new = max2(m_run[t], group_max(mx) * c_log2);
+      const float alpha = fast_exp2(m_run[t] - m_new);
+      m_run[t] = m_new;
+      l_run[t] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[t][dt] *= alpha;
+      prob_unit(t, 0, sr, pf, pl);
+      prob_unit(t, 1, sr, pf, pl);
+      ps[t] = pair_sum(t, pf, pl)[0];
+    });
+  };
+
+  f32x4 sc[NKP][NQT][2];       // scores of the current block, by key pair
+  T8 pprev[NQT], plprev[NQT];  // probabilities of the previous pair
+  if (nblk_w > 0) static_for<NKP>([&](auto P) { scores_pair(P, kaddr0, sc[decltype(P)::value]); });
+
+  // one block: FIRST skips the products of the (nonexistent) previous pair
+  auto block = [&](auto FIRST, int kb) __attribute__((always_inline)) {
+    constexpr bool first = decltype(FIRST)::value;
+    const int k0 = kb * BK;
+    const uint32_t kcur = kaddr0 + (uint32_t)(kb % NST) * kStage;
+    const uint32_t knext = kaddr0 + (uint32_t)((kb + 1) % NST) * kStage;
+    const uint32_t vcur = vaddr0 + (uint32_t)(kb % NST) * kStage;
+    const uint32_t vprev = vaddr0 + (uint32_t)((kb + NST - 1) % NST) * kStage;
+    // only blocks that straddle the key length or the diagonal are masked
+    const bool edge = (k0 + BK > L) || (causal && (k0 + BK - 1 > wq0));
+    if (edge) static_for<NKP>([&](auto P) { mask_pair(decltype(P)::value, k0, sc[decltype(P)::value]); });
+    static_for<NKP>([&](auto P) __attribute__((always_inline)) {
+      constexpr int p = decltype(P)::value;
+      constexpr int nvi = (first && p == 0) ? 0 : NDT;
+      constexpr int NS = nvi + NKC + 1;  // slots whose work may still read the old scores
+      constexpr int NU = 2 * NQT;        // work units (t, key tile), key tile 0 first
+      T8 pf[NQT], pl[NQT];
+      f32x4 psv[NQT];
+      // unit u = (t, hh) reads key tile hh of the old scores, which the K
+      // items of key tile hh overwrite (the first at slot nvi + NKC * hh):
+      // tile-0 units go in slots <= nvi, tile-1 units in slots <= nvi + NKC
+      auto work = [&](auto I) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value;
+        static_for<NU>([&](auto U) __attribute__((always_inline)) {
+          constexpr int u = decltype(U)::value;
+          constexpr int t = u % NQT, hh = u / NQT;
+          constexpr int slot = nvi == 0 ? 0 : u * NS / NU;
+          static_assert(slot <= nvi + NKC * hh, "a unit must read its scores before they are overwritten");
+          if constexpr (slot == i) {
+            prob_unit(t, hh, sc[p], pf, pl);
+            if constexpr (hh == 1) psv[t] = pair_sum(t, pf, pl);
+          }
+        });
+      };
+      // products of the previous pair, then the scores of pair p of block
+      // kb+1 (past the wave's last block: unused) into the registers the
+      // units release
+      stream(std::integral_constant<int, p == 0 ? NKP - 1 : p - 1>{}, std::integral_constant<int, nvi>{},
+             P, std::integral_constant<int, 2 * NKC>{}, p == 0 ? vprev : vcur, knext, pprev, plprev, sc[p],
+             work);
+      float ps[NQT];
+      if (__any(check(psv, ps))) redo(P, kcur, k0, edge, pf, pl, ps);
+#pragma unroll
+      for (int t = 0; t < NQT; ++t) {
+        l_run[t] += ps[t];
+        pprev[t] = pf[t];
+        if constexpr (kBf16) plprev[t] = pl[t];
+      }
+    });
+    if (kb == nblk_w - 1) {  // the wave's last block: products of its last pair now
+      f32x4 unused[NQT][2];
+      stream(std::integral_constant<int, NKP - 1>{}, std::integral_constant<int, NDT>{},
+             std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, vcur, 0u, pprev, plprev, unused,
+             no_work);
+    }
+  };
+
+  // block kb+1's copies (issued one block ago) have landed; after the
+  // barrier everyone's have, and everyone is done with block kb-2, whose
+  // stage the copy of block kb+2 reuses
+  wait_vmem();
+  block_barrier();
+  if (2 < nblk) dma_block(2, 2 * BK);
+  if (nblk_w > 0) block(std::true_type{}, 0);
+  for (int kb = 1; kb < nblk; ++kb) {
+    wait_vmem();
+    block_barrier();
+    if (kb + 2 < nblk) dma_block((kb + 2) % NST, (kb + 2) * BK);
+    if (kb >= nblk_w) continue;  // wave-uniform: block is past this wave's rows
+    block(std::false_type{}, kb);
+  }
+
+  // ---- epilogue: O / l rounded once to T; lse = ln(2) * (m + log2 l)
+  if (wave_live) {
+#pragma unroll
+    for (int t = 0; t < NQT; ++t) {
+      const float l = l_run[t];
+      const int row = wq0 + 16 * t + c;
+      const float inv = 1.f / l;  // l >= 1: the key that set the running max contributes 1
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        T4 ov;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[i] = to_t<T>(o[t][dt][i] * inv);
+        buf_store8(ov, ro, row * RO + (16 * dt + 4 * g) * 2);
+      }
+      if (LSEp) buf_store4((m_run[t] + fast_log2(l)) * kLn2, rl, g == 0 ? row * 4 : kOutOfRange);
+    }
+  }
+}
+
 template <typename T, int D, int NQT, int NW, int BK, bool SM, int NST = 2>
 static hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   constexpr int BQ = NW * NQT * 16;
@@ -376,9 +786,25 @@ static hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename T, int D, int NQT, int NW, int BK, int MINB>
+static hipError_t launch_pipe(const AttnParams& p, hipStream_t s) {
+  constexpr int BQ = NW * NQT * 16;
+  const int n_qblk = (p.S + BQ - 1) / BQ;
+  const int64_t n_wg = (int64_t)p.B * p.H * n_qblk;
+  if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((attn_fwd_pipe<T, D, NQT, NW, BK, MINB>), dim3((unsigned)n_wg), dim3(NW * 64), 0, s,
+                     (const T*)p.q, (const T*)p.k, (const T*)p.v, (T*)p.out, p.lse, p.key_len,
+                     p.H, p.S, p.causal, n_qblk, p.c_log2, p.lay);
+  return hipGetLastError();
+}
+
 // Tile shapes (NQT query tiles per wave, NW waves, BK keys per block, row sum
 // on the matrix cores) per head size. Entry 0 is the default; the others are
-// kept for A/B measurement and are selected with MHA_TILE_CONFIG.
+// kept for A/B measurement and are selected with MHA_TILE_CONFIG (entry 8 is
+// the unpipelined loop at the default's tile).
+template <typename T>
+constexpr bool kBf16T = __is_same(T, bf16_t);
+
 template <typename T>
 static hipError_t launch_general(const AttnParams& p, hipStream_t s) {
   const int cfg = p.tile_cfg;
@@ -386,16 +812,27 @@ static hipError_t launch_general(const AttnParams& p, hipStream_t s) {
     case 8: return launch_one<T, 8, 2, 4, 64, false>(p, s);
     case 16: return launch_one<T, 16, 2, 4, 64, false>(p, s);
     case 32: return launch_one<T, 32, 2, 4, 64, false>(p, s);
-    case 64:  // default: 4 waves of 64 query rows, two workgroups per CU
+    case 64:
+      // default: 4 waves of 64 query rows, two workgroups per CU; fp16 runs
+      // the pipelined loop (bf16's head + remainder probabilities do not fit
+      // its registers at this tile)
       if (cfg == 1) return launch_one<T, 64, 2, 8, 128, true>(p, s);
       if (cfg == 2) return launch_one<T, 64, 2, 8, 64, true, 3>(p, s);
       if (cfg == 3) return launch_one<T, 64, 2, 8, 64, false>(p, s);
       if (cfg == 4) return launch_one<T, 64, 2, 8, 64, true>(p, s);
       if (cfg == 5) return launch_one<T, 64, 2, 4, 64, true>(p, s);
-      return launch_one<T, 64, 4, 4, 64, true>(p, s);
-    case 128:
+      if (cfg == 6) return launch_pipe<T, 64, 2, 8, 64, 1>(p, s);
+      if (cfg == 7) return launch_pipe<T, 64, 3, 4, 64, 2>(p, s);
+      if constexpr (kBf16T<T>) {
+        return launch_one<T, 64, 4, 4, 64, true>(p, s);
+      } else {
+        if (cfg == 8) return launch_one<T, 64, 4, 4, 64, true>(p, s);
+        return launch_pipe<T, 64, 4, 4, 64, 2>(p, s);
+      }
+    case 128:  // default: pipelined, 8 waves of 32 query rows
       if (cfg == 1) return launch_one<T, 128, 2, 8, 64, true, 3>(p, s);
-      return launch_one<T, 128, 2, 8, 64, true>(p, s);
+      if (cfg == 8) return launch_one<T, 128, 2, 8, 64, true>(p, s);
+      return launch_pipe<T, 128, 2, 8, 64, 1>(p, s);
     case 256:
       if (cfg == 1) return launch_one<T, 256, 2, 8, 32, true, 3>(p, s);
       if (cfg == 2) return launch_one<T, 256, 2, 8, 32, true, 4>(p, s);

@@ -149,6 +149,28 @@ def test_adversarial_input_scales(mha, scale, D, S):
     check_full(out, lse, q, k, v, None, True, f"scale {scale} D={D}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal,L", [(False, None), (True, None), (False, 650), (True, 650)])
+def test_running_max_jumps(mha, D, causal, L):
+    """Scores that climb by about 20 log2 units every 32 keys, so a running
+    max taken from earlier keys is exceeded past the fp16 range at every key
+    pair, in the middle of blocks and across them (the general kernel's
+    overflow check and recompute path). With q = 1 along every axis and
+    k_j = a_j / sqrt(d_h) along every axis, q.k_j / sqrt(d_h) = a_j =
+    14 floor(j / 32) (+ noise)."""
+    B, H, S = 2, 2, 700
+    g = torch.Generator().manual_seed(3)
+    a = 14.0 * (torch.arange(S, dtype=torch.float64) // 32) + 0.5 * torch.randn(S, generator=g, dtype=torch.float64)
+    q = 1.0 + 0.05 * torch.randn(B, H, S, D, generator=g, dtype=torch.float64)
+    k = (a / math.sqrt(D))[:, None] + 0.05 * torch.randn(B, H, S, D, generator=g, dtype=torch.float64)
+    v = torch.randn(B, H, S, D, generator=g, dtype=torch.float64)
+    q, k, v = (t.half() for t in (q, k, v))
+    kl = None if L is None else torch.full((B,), L, dtype=torch.int32)
+    out, lse = run_gpu(mha, q, k, v, kl, causal, variant="mfma")
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    check_full(out, lse, q, k, v, kl, causal, f"climbing scores D={D} causal={causal} L={L}")
+
+
 def test_deterministic(mha):
     w = WORKLOADS["compute"].with_(B=2)
     q, k, v, kl = make_inputs(w, 5)

@@ -20,7 +20,12 @@
 // quotient is unchanged. Key blocks past the causal diagonal or the key
 // length are skipped; only blocks that straddle either boundary are masked.
 // The row sum l can be accumulated on the matrix cores (a ones operand times
-// the same rounded P as the numerator) instead of on the vector ALUs.
+// the same rounded P as the numerator) instead of on the vector ALUs. With
+// STALE the block maximum is not taken at all: probabilities use the running
+// max as it stands, and each key pair's matrix-core row sums are checked for
+// overflow of the dtype (the check and recompute of attn_fwd_pipe below; the
+// pair's scores are still in registers, so a failing pair only needs its own
+// maximum, a rescale and new probabilities).
 //
 // LDS layout. Rows are padded by one 16-byte slot (the DMA loads a zero
 // there), and rows are permuted inside each 32-key pair so every read is
@@ -42,6 +47,7 @@
 namespace mha {
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units: lazy rescale threshold
+constexpr float kNoMaxStale = -1.0e30f;  // finite: exp2(s c - it) overflows, exp2(-inf) stays 0
 
 // key (within a 32-key pair) stored at LDS row rho of the K / V tile
 __device__ __forceinline__ int k_key_of_row(int rho) {
@@ -54,7 +60,7 @@ __device__ __forceinline__ int v_key_of_row(int rho) {
 
 // Four-wave workgroups ask for two of them per CU (two waves per SIMD), which
 // also keeps matrix-core results in ordinary VGPRs.
-template <typename T, int D, int NQT, int NW, int BK, bool SUM_MFMA, int NST>
+template <typename T, int D, int NQT, int NW, int BK, bool SUM_MFMA, int NST, bool STALE = false>
 __global__ void __launch_bounds__(NW * 64, NW == 4 ? 2 : 1)
 attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
               T* __restrict__ Op, float* __restrict__ LSEp, const int32_t* __restrict__ key_len,
@@ -193,7 +199,7 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   f32x4 o[NQT][NDT], lsum[NQT];
 #pragma unroll
   for (int t = 0; t < NQT; ++t) {
-    m_run[t] = -INFINITY;
+    m_run[t] = STALE ? kNoMaxStale : -INFINITY;
     l_run[t] = 0.f;
     lsum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -237,14 +243,32 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
         const T4 kf = *(const T4*)(Ks + rbase + kread16);
 #pragma unroll
         for (int t = 0; t < NQT; ++t) s[t][kt] = mfma_k16(kf, qf4[t], s[t][kt]);
-      } else {
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-          const T8 kf = *(const T8*)(Ks + rbase + kread + 32 * kc);
-#pragma unroll
-          for (int t = 0; t < NQT; ++t) s[t][kt] = mfma_k32(kf, qf[t][kc], s[t][kt]);
-        }
       }
+    }
+    if constexpr (D > 16) {
+      // K fragments through inline asm, LAK reads ahead of their products
+      // (compiler-visible reads were issued two at a time and waited for at
+      // once, leaving the LDS latency exposed on every pair)
+      constexpr int NKI = NKT * NKC;
+      constexpr int LAK = NKI < 4 ? NKI : 4;
+      const uint32_t kaddr = lds_addr(Ks + kread);
+      u32x4 kfr[NKI];
+      auto kissue = [&](auto I) {
+        constexpr int i = decltype(I)::value;
+        constexpr int kt = i / NKC, kc = i % NKC;
+        kfr[i] = lds_read_b128_asm<((32 * (kt >> 1) + 16 * (kt & 1)) * STR + 32 * kc) * (int)sizeof(T)>(kaddr);
+      };
+      static_for<LAK>(kissue);
+      static_for<NKI>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        constexpr int kt = i / NKC, kc = i % NKC;
+        if constexpr (i + LAK < NKI) kissue(std::integral_constant<int, i + LAK>{});
+        constexpr int last = i + LAK < NKI ? i + LAK : NKI - 1;
+        lgkm_wait1<last - i>(kfr[i]);
+        const T8 kf = __builtin_bit_cast(T8, kfr[i]);
+#pragma unroll
+        for (int t = 0; t < NQT; ++t) s[t][kt] = mfma_k32(kf, qf[t][kc], s[t][kt]);
+      });
     }
 
     // ---- mask only blocks that straddle the key length or the diagonal:
@@ -265,31 +289,33 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
       }
     }
 
-    // ---- block row maxima; move the running max only when it is exceeded
-    //      by more than the slack (wave-uniform decision)
-    float mb[NQT];
-    bool grow = false;
-#pragma unroll
-    for (int t = 0; t < NQT; ++t) {
-      float mx = s[t][0][0];
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) {
-        mx = max3(mx, s[t][kt][0], s[t][kt][1]);
-        mx = max3(mx, s[t][kt][2], s[t][kt][3]);
-      }
-      mb[t] = group_max(mx) * c_log2;  // finite: key 0 is visible to every row
-      grow |= mb[t] > m_run[t] + kRescaleSlack;
-    }
-    if (__any(grow)) {
-#pragma unroll
+    if constexpr (!STALE) {
+      // ---- block row maxima; move the running max only when it is exceeded
+      //      by more than the slack (wave-uniform decision)
+      float mb[NQT];
+      bool grow = false;
+  #pragma unroll
       for (int t = 0; t < NQT; ++t) {
-        const float m_new = fmaxf(m_run[t], mb[t]);
-        const float alpha = fast_exp2(m_run[t] - m_new);
-        m_run[t] = m_new;
-        l_run[t] *= alpha;
-        lsum[t] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[t][dt] *= alpha;
+        float mx = s[t][0][0];
+  #pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+          mx = max3(mx, s[t][kt][0], s[t][kt][1]);
+          mx = max3(mx, s[t][kt][2], s[t][kt][3]);
+        }
+        mb[t] = group_max(mx) * c_log2;  // finite: key 0 is visible to every row
+        grow |= mb[t] > m_run[t] + kRescaleSlack;
+      }
+      if (__any(grow)) {
+  #pragma unroll
+        for (int t = 0; t < NQT; ++t) {
+          const float m_new = fmaxf(m_run[t], mb[t]);
+          const float alpha = fast_exp2(m_run[t] - m_new);
+          m_run[t] = m_new;
+          l_run[t] *= alpha;
+          lsum[t] *= alpha;
+  #pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) o[t][dt] *= alpha;
+        }
       }
     }
 
@@ -299,14 +325,15 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
     static_for<NKP>([&](auto P) {
       constexpr int p = decltype(P)::value;
       T8 pf[NQT], pl[NQT];
-#pragma unroll
-      for (int t = 0; t < NQT; ++t) {
+      // rounded probabilities of pair p for query tile t; returns their
+      // unrounded sum
+      auto probs = [&](int t) {
         float ls = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float a0 = fast_exp2(fmaf(s[t][2 * p][i], c_log2, -m_run[t]));
           const float a1 = fast_exp2(fmaf(s[t][2 * p + 1][i], c_log2, -m_run[t]));
-          if constexpr (!SUM_MFMA) ls += a0 + a1;
+          if constexpr (!SUM_MFMA && !STALE) ls += a0 + a1;
           pf[t][i] = to_t<T>(a0);
           pf[t][4 + i] = to_t<T>(a1);
           if constexpr (kBf16) {
@@ -314,11 +341,53 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
             pl[t][4 + i] = to_t<T>(a1 - to_f(pf[t][4 + i]));
           }
         }
-        if constexpr (SUM_MFMA) {
-          lsum[t] = mfma_k32(ones, pf[t], lsum[t]);
-          if constexpr (kBf16) lsum[t] = mfma_k32(ones, pl[t], lsum[t]);
-        } else {
-          l_run[t] += ls;
+        return ls;
+      };
+      if constexpr (STALE) {
+        // probabilities against the running max as it stands; the pair's
+        // matrix-core row sums are finite exactly when none overflowed the
+        // dtype (or was NaN). Otherwise move the max to the pair's maximum,
+        // rescale, and redo the pair (its scores are still in registers).
+        f32x4 ps[NQT];
+        bool bad = false;
+#pragma unroll
+        for (int t = 0; t < NQT; ++t) {
+          probs(t);
+          ps[t] = mfma_k32(ones, pf[t], f32x4{0.f, 0.f, 0.f, 0.f});
+          if constexpr (kBf16) ps[t] = mfma_k32(ones, pl[t], ps[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < NQT; ++t) bad |= !(ps[t][0] <= 3.0e38f);
+        if (__any(bad)) {
+#pragma unroll
+          for (int t = 0; t < NQT; ++t) {
+            float mx = max3(s[t][2 * p][0], s[t][2 * p][1], s[t][2 * p][2]);
+            mx = max3(mx, s[t][2 * p][3], s[t][2 * p + 1][0]);
+            mx = max3(mx, s[t][2 * p + 1][1], s[t][2 * p + 1][2]);
+            mx = max2(mx, s[t][2 * p + 1][3]);
+            const float m_new = max2(m_run[t], group_max(mx) * c_log2);
+            const float alpha = fast_exp2(m_run[t] - m_new);
+            m_run[t] = m_new;
+            l_run[t] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) o[t][dt] *= alpha;
+            probs(t);
+            ps[t] = mfma_k32(ones, pf[t], f32x4{0.f, 0.f, 0.f, 0.f});
+            if constexpr (kBf16) ps[t] = mfma_k32(ones, pl[t], ps[t]);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < NQT; ++t) l_run[t] += ps[t][0];  // every row holds query c's sum
+      } else {
+#pragma unroll
+        for (int t = 0; t < NQT; ++t) {
+          const float ls = probs(t);
+          if constexpr (SUM_MFMA) {
+            lsum[t] = mfma_k32(ones, pf[t], lsum[t]);
+            if constexpr (kBf16) lsum[t] = mfma_k32(ones, pl[t], lsum[t]);
+          } else {
+            l_run[t] += ls;
+          }
         }
       }
       constexpr int LA = NDT < 4 ? NDT : 4;
@@ -349,7 +418,7 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   if (wave_live) {
 #pragma unroll
     for (int t = 0; t < NQT; ++t) {
-      const float l = SUM_MFMA ? lsum[t][0] : group_sum(l_run[t]);
+      const float l = STALE ? l_run[t] : SUM_MFMA ? lsum[t][0] : group_sum(l_run[t]);
       const int row = wq0 + 16 * t + c;
       const float inv = 1.f / l;  // l >= 1: the running max's own key contributes 1
 #pragma unroll
@@ -774,13 +843,13 @@ attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   }
 }
 
-template <typename T, int D, int NQT, int NW, int BK, bool SM, int NST = 2>
+template <typename T, int D, int NQT, int NW, int BK, bool SM, int NST = 2, bool STALE = false>
 static hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   constexpr int BQ = NW * NQT * 16;
   const int n_qblk = (p.S + BQ - 1) / BQ;
   const int64_t n_wg = (int64_t)p.B * p.H * n_qblk;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_fwd_mfma<T, D, NQT, NW, BK, SM, NST>), dim3((unsigned)n_wg), dim3(NW * 64), 0, s,
+  hipLaunchKernelGGL((attn_fwd_mfma<T, D, NQT, NW, BK, SM, NST, STALE>), dim3((unsigned)n_wg), dim3(NW * 64), 0, s,
                      (const T*)p.q, (const T*)p.k, (const T*)p.v, (T*)p.out, p.lse, p.key_len,
                      p.H, p.S, p.causal, n_qblk, p.c_log2, p.lay);
   return hipGetLastError();
@@ -833,11 +902,17 @@ static hipError_t launch_general(const AttnParams& p, hipStream_t s) {
       if (cfg == 1) return launch_one<T, 128, 2, 8, 64, true, 3>(p, s);
       if (cfg == 8) return launch_one<T, 128, 2, 8, 64, true>(p, s);
       return launch_pipe<T, 128, 2, 8, 64, 1>(p, s);
-    case 256:
+    case 256:  // default: fp16 takes probabilities against the running max
+               // with the overflow check (bf16 spills with it)
       if (cfg == 1) return launch_one<T, 256, 2, 8, 32, true, 3>(p, s);
       if (cfg == 2) return launch_one<T, 256, 2, 8, 32, true, 4>(p, s);
       if (cfg == 3) return launch_one<T, 256, 2, 8, 32, false>(p, s);
-      return launch_one<T, 256, 2, 8, 32, true>(p, s);
+      if constexpr (kBf16T<T>) {
+        return launch_one<T, 256, 2, 8, 32, true>(p, s);
+      } else {
+        if (cfg == 8) return launch_one<T, 256, 2, 8, 32, true>(p, s);
+        return launch_one<T, 256, 2, 8, 32, true, 2, true>(p, s);
+      }
   }
   return hipErrorInvalidValue;
 }

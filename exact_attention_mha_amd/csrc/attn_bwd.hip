@@ -263,15 +263,33 @@ __device__ __forceinline__ void bwd_dq_body(
       const bool edge = (k0 + BK > L) || (causal && (k0 + BK - 1 > wq0));
       T8 dsf[NQT][NKP], dsl[NQT][NKP];
 #pragma unroll
+      for (int t = 0; t < NQT; ++t)
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[t][kt][i] = fast_exp2(fmaf(s[t][kt][i], c_log2, nlse2[t]));
+      // hidden pairs get P = 0, only in blocks that reach a boundary (the
+      // empty asm keeps this a branch rather than a select on every element)
+      if (edge) {
+        asm volatile("");
+#pragma unroll
+        for (int t = 0; t < NQT; ++t) {
+          const int row = wq0 + 16 * t + c;
+          const int lim = (causal ? min(L - 1, row) : L - 1) - k0 - 4 * g;  // max visible key offset
+#pragma unroll
+          for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (16 * kt + i > lim) s[t][kt][i] = 0.f;
+        }
+      }
+#pragma unroll
       for (int t = 0; t < NQT; ++t) {
-        const int row = wq0 + 16 * t + c;
-        const int lim = (causal ? min(L - 1, row) : L - 1) - k0 - 4 * g;  // max visible key offset
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float p = fast_exp2(fmaf(s[t][kt][i], c_log2, nlse2[t]));
-            if (edge && 16 * kt + i > lim) p = 0.f;
+            const float p = s[t][kt][i];
             if constexpr (MODE == kRowPass) {
               drow[t] = fmaf(p, dp[t][kt][i], drow[t]);
               continue;
@@ -504,15 +522,29 @@ __device__ __forceinline__ void bwd_dkv_body(
           const f32x4 lv = *(const f32x4*)(ls + qr);
           const f32x4 dv = *(const f32x4*)(ds + qr);
 #pragma unroll
+          for (int t = 0; t < NKTW; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[h][t][i] = fast_exp2(fmaf(s[h][t][i], c_log2, -lv[i] * kLog2e));
+          // hidden pairs get P = 0, only in blocks that reach a boundary (the
+          // empty asm keeps this a branch: if-converted, every element of
+          // every block paid for the mask)
+          if (edge) {
+            asm volatile("");
+#pragma unroll
+            for (int t = 0; t < NKTW; ++t) {
+              const int key = wk0 + 16 * t + c;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int q = q0 + qr + i;
+                if (q >= S || key >= L || (causal && key > q)) s[h][t][i] = 0.f;
+              }
+            }
+          }
+#pragma unroll
           for (int t = 0; t < NKTW; ++t) {
-            const int key = wk0 + 16 * t + c;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              float pr = fast_exp2(fmaf(s[h][t][i], c_log2, -lv[i] * kLog2e));
-              if (edge) {
-                const int q = q0 + qr + i;
-                if (q >= S || key >= L || (causal && key > q)) pr = 0.f;
-              }
+              const float pr = s[h][t][i];
               const float d = pr * (dp[h][t][i] - dv[i]);
               const T ph = to_t<T>(pr), dh = to_t<T>(d);
               pf[t][4 * h + i] = ph;

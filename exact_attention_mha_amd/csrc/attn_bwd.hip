@@ -286,19 +286,29 @@ __device__ __forceinline__ void bwd_dq_body(
 #pragma unroll
       for (int t = 0; t < NQT; ++t) {
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
+        for (int kt = 0; kt < NKT; ++kt) {
+          if constexpr (MODE == kRowPass) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p = s[t][kt][i];
-            if constexpr (MODE == kRowPass) {
-              drow[t] = fmaf(p, dp[t][kt][i], drow[t]);
-              continue;
-            }
-            const float d = p * (dp[t][kt][i] - drow[t]);
-            const T dh = to_t<T>(d);
-            dsf[t][kt >> 1][4 * (kt & 1) + i] = dh;
-            if constexpr (kBf16) dsl[t][kt >> 1][4 * (kt & 1) + i] = to_t<T>(d - to_f(dh));
+            for (int i = 0; i < 4; ++i) drow[t] = fmaf(s[t][kt][i], dp[t][kt][i], drow[t]);
+            continue;
           }
+          // dS rounded two at a time (bf16 as head + remainder): words
+          // 2 (kt % 2), 2 (kt % 2) + 1 of the pair's operand
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const float d0 = s[t][kt][2 * j] * (dp[t][kt][2 * j] - drow[t]);
+            const float d1 = s[t][kt][2 * j + 1] * (dp[t][kt][2 * j + 1] - drow[t]);
+            const int w = 2 * (kt & 1) + j;
+            if constexpr (kBf16) {
+              uint32_t dh, dlo;
+              split2_bf16(d0, d1, dh, dlo);
+              set_word(dsf[t][kt >> 1], w, dh);
+              set_word(dsl[t][kt >> 1], w, dlo);
+            } else {
+              set_word(dsf[t][kt >> 1], w, pack2<T>(d0, d1));
+            }
+          }
+        }
       }
 
       // dQ^T += K^T dS^T, one key pair at a time
@@ -540,18 +550,26 @@ __device__ __forceinline__ void bwd_dkv_body(
               }
             }
           }
+          // rounded two at a time (one packed conversion per pair; bf16 as
+          // head + remainder): words 2h, 2h + 1 of each operand
 #pragma unroll
           for (int t = 0; t < NKTW; ++t) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float pr = s[h][t][i];
-              const float d = pr * (dp[h][t][i] - dv[i]);
-              const T ph = to_t<T>(pr), dh = to_t<T>(d);
-              pf[t][4 * h + i] = ph;
-              dsf[t][4 * h + i] = dh;
+            for (int j = 0; j < 2; ++j) {
+              const float p0 = s[h][t][2 * j], p1 = s[h][t][2 * j + 1];
+              const float d0 = p0 * (dp[h][t][2 * j] - dv[2 * j]);
+              const float d1 = p1 * (dp[h][t][2 * j + 1] - dv[2 * j + 1]);
               if constexpr (kBf16) {
-                pl[t][4 * h + i] = to_t<T>(pr - to_f(ph));
-                dsl[t][4 * h + i] = to_t<T>(d - to_f(dh));
+                uint32_t ph, plo, dh, dlo;
+                split2_bf16(p0, p1, ph, plo);
+                split2_bf16(d0, d1, dh, dlo);
+                set_word(pf[t], 2 * h + j, ph);
+                set_word(pl[t], 2 * h + j, plo);
+                set_word(dsf[t], 2 * h + j, dh);
+                set_word(dsl[t], 2 * h + j, dlo);
+              } else {
+                set_word(pf[t], 2 * h + j, pack2<T>(p0, p1));
+                set_word(dsf[t], 2 * h + j, pack2<T>(d0, d1));
               }
             }
           }

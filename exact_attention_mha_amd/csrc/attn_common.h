@@ -234,6 +234,34 @@ template <> __device__ __forceinline__ bf16_t to_t<bf16_t>(float x) { return (bf
 
 template <typename T> __device__ __forceinline__ float to_f(T x) { return (float)x; }
 
+// ---- pairs of floats rounded to 16-bit words (one packed conversion each) ----
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// (a, b) rounded to T, a in the low half
+template <typename T> __device__ __forceinline__ uint32_t pack2(float a, float b);
+template <> __device__ __forceinline__ uint32_t pack2<f16_t>(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+template <> __device__ __forceinline__ uint32_t pack2<bf16_t>(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+// bf16 head + remainder of a pair: hi = (a, b) rounded to bf16, lo = the
+// rounding errors (a - head_a, b - head_b) rounded to bf16 (exact
+// subtractions: the heads are a's and b's leading bits)
+__device__ __forceinline__ void split2_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack2<bf16_t>(a, b);
+  const float ha = __builtin_bit_cast(float, hi << 16);
+  const float hb = __builtin_bit_cast(float, hi & 0xffff0000u);
+  lo = pack2<bf16_t>(a - ha, b - hb);
+}
+// word j of an 8 x 16-bit operand
+template <typename V> __device__ __forceinline__ void set_word(V& v, int j, uint32_t w) {
+  u32x4 u = __builtin_bit_cast(u32x4, v);
+  u[j] = w;
+  v = __builtin_bit_cast(V, u);
+}
+
 template <typename V> __device__ __forceinline__ V zero_vec() {
   V z;
 #pragma unroll

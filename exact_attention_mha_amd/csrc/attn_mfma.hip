@@ -329,16 +329,30 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
       // unrounded sum
       auto probs = [&](int t) {
         float ls = 0.f;
+        if constexpr (kBf16) {
+          float a[8];  // elements 0..3: key tile 2p, 4..7: key tile 2p + 1
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float a0 = fast_exp2(fmaf(s[t][2 * p][i], c_log2, -m_run[t]));
-          const float a1 = fast_exp2(fmaf(s[t][2 * p + 1][i], c_log2, -m_run[t]));
-          if constexpr (!SUM_MFMA && !STALE) ls += a0 + a1;
-          pf[t][i] = to_t<T>(a0);
-          pf[t][4 + i] = to_t<T>(a1);
-          if constexpr (kBf16) {
-            pl[t][i] = to_t<T>(a0 - to_f(pf[t][i]));
-            pl[t][4 + i] = to_t<T>(a1 - to_f(pf[t][4 + i]));
+          for (int i = 0; i < 4; ++i) {
+            a[i] = fast_exp2(fmaf(s[t][2 * p][i], c_log2, -m_run[t]));
+            a[4 + i] = fast_exp2(fmaf(s[t][2 * p + 1][i], c_log2, -m_run[t]));
+            if constexpr (!SUM_MFMA && !STALE) ls += a[i] + a[4 + i];
+          }
+          // head + remainder, rounded two at a time
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            uint32_t hi, lo;
+            split2_bf16(a[2 * w], a[2 * w + 1], hi, lo);
+            set_word(pf[t], w, hi);
+            set_word(pl[t], w, lo);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float a0 = fast_exp2(fmaf(s[t][2 * p][i], c_log2, -m_run[t]));
+            const float a1 = fast_exp2(fmaf(s[t][2 * p + 1][i], c_log2, -m_run[t]));
+            if constexpr (!SUM_MFMA && !STALE) ls += a0 + a1;
+            pf[t][i] = to_t<T>(a0);
+            pf[t][4 + i] = to_t<T>(a1);
           }
         }
         return ls;
@@ -613,11 +627,21 @@ attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   // rounded probabilities of key tile hh of one pair for query tile t
   auto prob_unit = [&](int t, int hh, const f32x4 (&sp)[NQT][2], T8 (&pf)[NQT], T8 (&pl)[NQT])
       __attribute__((always_inline)) {
+    if constexpr (kBf16) {
+      // head + remainder, rounded two at a time: words 2hh, 2hh + 1
+      float a[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = fast_exp2(fmaf(sp[t][hh][i], c_log2, -m_run[t]));
-      pf[t][4 * hh + i] = to_t<T>(a);
-      if constexpr (kBf16) pl[t][4 * hh + i] = to_t<T>(a - to_f(pf[t][4 * hh + i]));
+      for (int i = 0; i < 4; ++i) a[i] = fast_exp2(fmaf(sp[t][hh][i], c_log2, -m_run[t]));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        uint32_t hi, lo;
+        split2_bf16(a[2 * j], a[2 * j + 1], hi, lo);
+        set_word(pf[t], 2 * hh + j, hi);
+        set_word(pl[t], 2 * hh + j, lo);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pf[t][4 * hh + i] = to_t<T>(fast_exp2(fmaf(sp[t][hh][i], c_log2, -m_run[t])));
     }
   };
   auto probs = [&](const f32x4 (&sp)[NQT][2], T8 (&pf)[NQT], T8 (&pl)[NQT]) __attribute__((always_inline)) {

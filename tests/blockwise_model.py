@@ -40,6 +40,78 @@ def _round_to(x: np.ndarray, dtype: str) -> np.ndarray:
     return x.astype(np.float32)
 
 
+def running_max_attention(q, k, v, causal=False, key_len=None, BQ=64, PAIR=32,
+                          emulate=False, dtype="f16", limit=65504.0, stats=None):
+    """The loop with probabilities taken against the running max as it stands
+    (no per-block maximum): each chunk of PAIR keys gets p = exp(s c - m); a
+    row whose chunk has a probability above `limit` (the input dtype's range;
+    the kernels detect it as a non-finite matrix-core row sum) or not finite
+    moves m to the chunk's maximum, rescales O and l by exp(m_old - m_new),
+    and redoes the chunk. m starts at a finite sentinel (-1e30) so the first
+    visible keys of a row always take that path. Same return values as
+    tiled_attention; `stats`, if a dict, receives the number of redone
+    (row, chunk) pairs under "redo"."""
+    q = np.asarray(q); k = np.asarray(k); v = np.asarray(v)
+    B, H, S, D = q.shape
+    kl = np.full(B, S) if key_len is None else np.clip(np.asarray(key_len).reshape(-1), 0, S)
+    ft = np.float32 if emulate else np.float64
+    c = ft(LOG2E / math.sqrt(D)) if emulate else 1.0 / math.sqrt(D)
+    expf = (lambda x: np.exp2(x.astype(ft)).astype(ft)) if emulate else np.exp
+    sentinel = ft(-1e30)
+    out = np.zeros((B, H, S, D))
+    lse = np.full((B, H, S), -np.inf)
+    redo = 0
+    with np.errstate(over="ignore", invalid="ignore"):
+        for b in range(B):
+            L = int(kl[b])
+            for h in range(H):
+                Q = q[b, h].astype(ft); K = k[b, h].astype(ft); V = v[b, h].astype(ft)
+                for q0 in range(0, S, BQ):
+                    q1 = min(S, q0 + BQ)
+                    rows = np.arange(q0, q1)
+                    kend = min(L, q1) if causal else L
+                    m = np.full(q1 - q0, sentinel, dtype=ft)
+                    l = np.zeros(q1 - q0, dtype=ft)
+                    acc = np.zeros((q1 - q0, D), dtype=ft)
+                    for k0 in range(0, kend, PAIR):
+                        k1 = min(kend, k0 + PAIR)
+                        s = (Q[q0:q1] @ K[k0:k1].T).astype(ft)
+                        vis = np.ones((q1 - q0, k1 - k0), dtype=bool)
+                        if causal:
+                            vis &= np.arange(k0, k1)[None, :] <= rows[:, None]
+                        s = np.where(vis, s, -np.inf).astype(ft)
+
+                        def probs():
+                            p = expf(s * c - m[:, None])
+                            p = np.where(vis, p, 0).astype(ft)
+                            return _round_to(p, dtype).astype(ft) if emulate else p
+
+                        p = probs()
+                        bad = ~np.all(np.isfinite(p) & (p <= limit), axis=1)
+                        if bad.any():
+                            redo += int(bad.sum())
+                            m_new = np.where(bad, np.maximum(m, (s.max(axis=1) * c).astype(ft)), m).astype(ft)
+                            alpha = expf(m - m_new)
+                            acc = (alpha[:, None] * acc).astype(ft)
+                            l = (alpha * l).astype(ft)
+                            m = m_new
+                            p = probs()
+                        l = (l + p.sum(axis=1)).astype(ft)
+                        acc = (acc + p @ V[k0:k1]).astype(ft)
+                    has = l > 0
+                    o = np.where(has[:, None], acc / np.where(has, l, 1)[:, None], 0)
+                    if emulate:
+                        o = _round_to(o.astype(np.float32), "bf16" if dtype == "bf16x2" else dtype)
+                        lg = np.where(has, (m + np.log2(np.where(has, l, 1))) / LOG2E, -np.inf)
+                    else:
+                        lg = np.where(has, m + np.log(np.where(has, l, 1)), -np.inf)
+                    out[b, h, q0:q1] = o
+                    lse[b, h, q0:q1] = lg
+    if stats is not None:
+        stats["redo"] = redo
+    return out, lse
+
+
 def tiled_attention(q, k, v, causal=False, key_len=None, BQ=64, BK=64,
                     emulate=False, dtype="f16"):
     """Online-softmax attention over [B,H,S,D] arrays, one query tile at a time.

@@ -8,12 +8,14 @@ softmax(QK^T / sqrt(d_k)) V in exact arithmetic). With the kernels' precision
 emulated, it also predicts how much of the error budget the GPU should use.
 """
 
+import math
+
 import numpy as np
 import pytest
 import torch
 
 from oracle import attention, budget_fraction, gate
-from blockwise_model import tiled_attention
+from blockwise_model import running_max_attention, tiled_attention
 
 
 @pytest.mark.parametrize("BQ,BK", [(1, 1), (7, 16), (16, 32), (32, 7), (64, 64), (128, 128)])
@@ -67,3 +69,69 @@ def test_single_bf16_probability_rounding_is_too_coarse():
         o, _ = tiled_attention(q, k, v, causal=True, emulate=True, dtype="bf16")
         worst = max(worst, budget_fraction(o, ref_o))
     assert worst > 0.6
+
+
+def _climbing(S, D, seed, step=14.0):
+    """Scores climbing by `step` (natural units; x1.44 in log2 units) every
+    32 keys: q = 1 along every axis, k_j = a_j / sqrt(D) along every axis."""
+    rng = np.random.default_rng(seed)
+    a = step * (np.arange(S) // 32) + 0.5 * rng.standard_normal(S)
+    q = 1.0 + 0.05 * rng.standard_normal((1, 2, S, D))
+    k = (a / math.sqrt(D))[None, None, :, None] + 0.05 * rng.standard_normal((1, 2, S, D))
+    v = rng.standard_normal((1, 2, S, D))
+    return q, k, v
+
+
+@pytest.mark.parametrize("BQ,PAIR", [(1, 1), (16, 32), (64, 32), (33, 7)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("inputs", ["normal", "climbing"])
+def test_running_max_loop_equals_definition(BQ, PAIR, causal, inputs):
+    """Probabilities against the running max with an overflow check and
+    recompute reach the definition to float64 rounding, also when the row
+    maximum climbs past the limit at every chunk (redo on most chunks)."""
+    B, H, S, D = 1, 2, 150, 8
+    if inputs == "normal":
+        rng = np.random.default_rng(BQ * 100 + PAIR)
+        q, k, v = (rng.standard_normal((B, H, S, D)) for _ in range(3))
+    else:
+        q, k, v = _climbing(S, D, seed=PAIR)
+    kl = [137]
+    ref_o, ref_l = attention(q, k, v, causal=causal, key_len=kl)
+    st = {}
+    o, l = running_max_attention(q, k, v, causal=causal, key_len=kl, BQ=BQ, PAIR=PAIR, stats=st)
+    np.testing.assert_allclose(o, ref_o, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(l, ref_l, rtol=1e-11, atol=1e-12)
+    assert st["redo"] > 0  # at least the first visible keys of every row
+
+
+def test_running_max_redoes_only_when_needed():
+    """With N(0, 1) scores the running max from the first chunk holds (no
+    redo after it); with scores climbing ~20 log2 units per 32 keys almost
+    every chunk is redone."""
+    B, H, S, D = 1, 2, 256, 64
+    rng = np.random.default_rng(0)
+    q, k, v = (rng.standard_normal((B, H, S, D)) for _ in range(3))
+    st = {}
+    running_max_attention(q, k, v, BQ=64, PAIR=32, stats=st)
+    assert st["redo"] == B * H * S  # each row once, at its first chunk
+    q, k, v = _climbing(S, D, seed=1)
+    st = {}
+    running_max_attention(q, k, v, BQ=64, PAIR=32, stats=st)
+    assert st["redo"] >= B * H * S * (S // 32 - 1)
+
+
+@pytest.mark.parametrize("inputs", ["normal", "climbing"])
+def test_running_max_emulated_precision_budget(inputs):
+    """fp16 probabilities against a stale running max (values up to the fp16
+    maximum keep their relative precision) stay well inside the budget."""
+    B, H, S, D = 1, 2, 256, 64
+    if inputs == "normal":
+        g = torch.Generator().manual_seed(0)
+        q, k, v = (torch.randn(B, H, S, D, generator=g).half().double().numpy() for _ in range(3))
+    else:
+        q, k, v = (torch.from_numpy(t).half().double().numpy() for t in _climbing(S, D, seed=2))
+    ref_o, ref_l = attention(q, k, v, causal=True)
+    o, l = running_max_attention(q, k, v, causal=True, BQ=64, PAIR=32, emulate=True, dtype="f16")
+    assert budget_fraction(o, ref_o) < 0.5
+    assert budget_fraction(l, ref_l) < 0.05
+    assert gate(o, ref_o).all()

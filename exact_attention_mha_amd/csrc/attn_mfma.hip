@@ -48,6 +48,10 @@ namespace mha {
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units: lazy rescale threshold
 constexpr float kNoMaxStale = -1.0e30f;  // finite: exp2(s c - it) overflows, exp2(-inf) stays 0
+// largest accepted row sum of one 32-key pair's rounded probabilities: above
+// every sum of 32 finite fp16 values (32 * 65504 < 2^21), below any that
+// holds an overflowed one; for bf16 it bounds each probability by 2^21
+constexpr float kPairSumMax = 2097152.0f;
 
 // key (within a 32-key pair) stored at LDS row rho of the K / V tile
 __device__ __forceinline__ int k_key_of_row(int rho) {
@@ -359,8 +363,8 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
       };
       if constexpr (STALE) {
         // probabilities against the running max as it stands; the pair's
-        // matrix-core row sums are finite exactly when none overflowed the
-        // dtype (or was NaN). Otherwise move the max to the pair's maximum,
+        // matrix-core row sums stay within kPairSumMax exactly when no fp16
+        // probability overflowed (or was NaN). Otherwise move the max to the pair's maximum,
         // rescale, and redo the pair (its scores are still in registers).
         f32x4 ps[NQT];
         bool bad = false;
@@ -371,7 +375,7 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
           if constexpr (kBf16) ps[t] = mfma_k32(ones, pl[t], ps[t]);
         }
 #pragma unroll
-        for (int t = 0; t < NQT; ++t) bad |= !(ps[t][0] <= 3.0e38f);
+        for (int t = 0; t < NQT; ++t) bad |= !(ps[t][0] <= kPairSumMax);
         if (__any(bad)) {
 #pragma unroll
           for (int t = 0; t < NQT; ++t) {
@@ -453,17 +457,19 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
 //
 // Probabilities of a key pair use the running max as it stands, without first
 // taking the block's own maximum: p = exp2(s c - m) only has to be checked
-// for overflow. The matrix-core row sum of the pair (ones times the rounded
-// probabilities, which the denominator needs anyway) is finite exactly when
-// no probability of the pair overflowed the input dtype or was NaN. A pair
-// that fails -- the first visible keys of a row, or a row whose maximum
-// jumped by more than the dtype's range (2^16 for fp16) -- recomputes its
-// scores, moves the running max to their maximum, rescales O and l by
-// exp2(m_old - m_new) and redoes its probabilities. Numerator and denominator
-// always share one max, so the quotient is that of the online-softmax
-// recurrence (devpost "gpu-transformer-optimization", section 2.1); rounded
-// probabilities keep their relative precision at any magnitude below the
-// dtype's maximum.
+// for size. The matrix-core row sum of the pair (ones times the rounded
+// probabilities, which the denominator needs anyway) is checked against
+// kPairSumMax = 2^21: a probability that overflowed fp16 (or is NaN) fails
+// it, every sum of 32 finite fp16 probabilities passes, and for bf16 (whose
+// probabilities only overflow at the fp32 range) it keeps every probability
+// below 2^21, so O and l stay far from fp32 overflow. A pair that fails --
+// the first visible keys of a row, or a row whose maximum jumped by more than
+// about 16 (fp16) or 21 (bf16) log2 units -- recomputes its scores, moves the
+// running max to their maximum, rescales O and l by exp2(m_old - m_new) and
+// redoes its probabilities. Numerator and denominator always share one max,
+// so the quotient is that of the online-softmax recurrence (devpost
+// "gpu-transformer-optimization", section 2.1); rounded probabilities keep
+// their relative precision at any magnitude below that bound.
 //
 // The loop is software pipelined: the step for key pair p of block kb issues,
 // in one stretch of straight-line code,
@@ -657,14 +663,14 @@ attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
     if constexpr (kBf16) a = mfma_k32(ones, pl[t], a);
     return a;
   };
-  // true if any sum is not finite; ps takes query c's sum (every row of the
-  // product holds it)
+  // true if any sum exceeds kPairSumMax or is NaN; ps takes query c's sum
+  // (every row of the product holds it)
   auto check = [&](const f32x4 (&psv)[NQT], float (&ps)[NQT]) __attribute__((always_inline)) {
     bool bad = false;
 #pragma unroll
     for (int t = 0; t < NQT; ++t) {
       ps[t] = psv[t][0];
-      bad |= !(ps[t] <= 3.0e38f);
+      bad |= !(ps[t] <= kPairSumMax);
     }
     return bad;
   };

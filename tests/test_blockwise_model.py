@@ -135,3 +135,24 @@ def test_running_max_emulated_precision_budget(inputs):
     assert budget_fraction(o, ref_o) < 0.5
     assert budget_fraction(l, ref_l) < 0.05
     assert gate(o, ref_o).all()
+
+
+def test_running_max_bf16_needs_a_bound_not_just_a_finiteness_test():
+    """bf16 probabilities only overflow at the fp32 range, so a check that
+    only rejects infinite sums lets probabilities near 2^127 through while
+    the running max is far behind, and O / l then overflow fp32 (scores
+    spread over hundreds of log2 units: inputs scaled by 12). Bounding the
+    probabilities by 2^21 (the kernels bound each 32-key pair's sum, which
+    bounds every probability in it) keeps the result inside the rule."""
+    B, H, S, D = 1, 2, 396, 128
+    g = torch.Generator().manual_seed(144)
+    q, k, v = (torch.randn(B, H, S, D, generator=g) for _ in range(3))
+    q, k = (t * 12.0 for t in (q, k))
+    q, k, v = (t.bfloat16().double().numpy() for t in (q, k, v))
+    ref_o, ref_l = attention(q, k, v, causal=True)
+    o, l = running_max_attention(q, k, v, causal=True, BQ=64, PAIR=32, emulate=True,
+                                 dtype="bf16x2", limit=np.inf)
+    assert not np.isfinite(o).all()
+    o, l = running_max_attention(q, k, v, causal=True, BQ=64, PAIR=32, emulate=True,
+                                 dtype="bf16x2", limit=2.0 ** 21)
+    assert np.isfinite(o).all() and gate(o, ref_o).all() and gate(l, ref_l).all()

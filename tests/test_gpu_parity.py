@@ -137,21 +137,27 @@ def test_padded_keys_never_read(mha, variant):
 
 
 @pytest.mark.parametrize("scale", [1e-3, 10.0, 30.0])
-@pytest.mark.parametrize("D,S", [(64, 300), (256, 130), (16, 128)])
-def test_adversarial_input_scales(mha, scale, D, S):
+@pytest.mark.parametrize("D,S,dt", [(64, 300, "f16"), (256, 130, "f16"), (16, 128, "f16"),
+                                    (128, 396, "bf16"), (64, 300, "bf16")])
+def test_adversarial_input_scales(mha, scale, D, S, dt):
+    """Scores spread over hundreds of log2 units: the running max is
+    exceeded by huge margins (bf16 probabilities would stay finite in fp32
+    far past the point where O overflows, so the overflow check must bound
+    them, not just test for infinity)."""
     from workloads import Workload
-    w = Workload("adv", 2, 2, S, D, torch.float16, True, None)
+    w = Workload("adv", 2, 2, S, D, _DT[dt], True, None)
     q, k, v, _ = make_inputs(w, 11)
-    q = (q.float() * scale).half()
-    k = (k.float() * scale).half()
+    q = (q.float() * scale).to(_DT[dt])
+    k = (k.float() * scale).to(_DT[dt])
     out, lse = run_gpu(mha, q, k, v, None, True)
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
     check_full(out, lse, q, k, v, None, True, f"scale {scale} D={D}")
 
 
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal,L", [(False, None), (True, None), (False, 650), (True, 650)])
-def test_running_max_jumps(mha, D, causal, L):
+def test_running_max_jumps(mha, dt, D, causal, L):
     """Scores that climb by about 20 log2 units every 32 keys, so a running
     max taken from earlier keys is exceeded past the fp16 range at every key
     pair, in the middle of blocks and across them (the general kernel's
@@ -164,7 +170,7 @@ def test_running_max_jumps(mha, D, causal, L):
     q = 1.0 + 0.05 * torch.randn(B, H, S, D, generator=g, dtype=torch.float64)
     k = (a / math.sqrt(D))[:, None] + 0.05 * torch.randn(B, H, S, D, generator=g, dtype=torch.float64)
     v = torch.randn(B, H, S, D, generator=g, dtype=torch.float64)
-    q, k, v = (t.half() for t in (q, k, v))
+    q, k, v = (t.to(_DT[dt]) for t in (q, k, v))
     kl = None if L is None else torch.full((B,), L, dtype=torch.int32)
     out, lse = run_gpu(mha, q, k, v, kl, causal, variant="mfma")
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()

@@ -196,10 +196,12 @@ def backward(q, k, v, out, lse, dout, causal: bool = False, key_len=None,
     Args:
       q, k, v, causal, key_len: exactly as passed to forward(); all
         contiguous here, k and v with H or H_kv (dividing H) heads.
-      out, lse: forward()'s outputs for those inputs (lse is required).
+      out, lse: forward()'s outputs for those inputs (lse is required; out
+        is checked for shape and dtype but not read).
       dout: the output gradient, contiguous [B, H, S, d_h], dtype of q.
       dq, dk, dv: optional preallocated outputs shaped like q, k, v.
-      delta: optional float32 [B, H, S] workspace; receives rowsum(dout * out).
+      delta: optional float32 [B, H, S] workspace; receives the row term
+        rowsum(P * dP), i.e. rowsum(dout * O) for the exact output O.
       stream: a torch.cuda.Stream (default: the current stream).
     Returns:
       (dq, dk, dv).

@@ -2,21 +2,20 @@
 // accumulation): dQ, dK, dV of sum(dO * O) for O = softmax(Q K^T / sqrt(d_h)
 // + mask) V.
 //
-// Two kernels, as in the fused backward of rustingstudio "brain/docs/baseline"
-// ("Fused attention"): the query gradient is complete inside a query tile and
-// the key / value gradients inside a key tile, so
-//   * attn_bwd_dq   walks key blocks for a block of query rows, and
-//   * attn_bwd_dkv  walks query blocks for a block of key rows,
+// Two kinds of work, as in the fused backward of rustingstudio
+// "brain/docs/baseline" ("Fused attention"): the query gradient is complete
+// inside a query tile and the key / value gradients inside a key tile, so
+//   * the dq body walks key blocks for a block of query rows, and
+//   * the dkv body walks query blocks for a block of key rows,
 // and both rebuild the probabilities from the stored log-sum-exp instead of
 // keeping them: P = exp(S / sqrt(d_h) - lse). With dP = dO V^T and the row
 // term D = rowsum(dO * O) (equal to rowsum(P * dP) since O = P V),
 //   dS = P * (dP - D),  dQ = dS K / sqrt(d_h),  dK = dS^T Q / sqrt(d_h),
 //   dV = P^T dO.
-// D goes through the caller's workspace: for fp16 the dq kernel computes it
-// from dO and the forward's output and writes it; for bf16 a first pass of
-// the dq kernel accumulates rowsum(P * dP) exactly and writes it, and the dq
-// pass proper reads it. The dkv kernel, launched after them on the same
-// stream, reads it.
+// D goes through the caller's workspace: a first pass of the dq body
+// (attn_bwd_dq) accumulates rowsum(P * dP) in fp32 and writes it, then one
+// launch (attn_bwd_both) runs the dq body proper and the dkv body, both
+// reading it. The forward's rounded output is not used for D.
 //
 // Products are formed transposed where that puts the contraction index in
 // the operand registers directly (lane = 16g + c):
@@ -27,9 +26,11 @@
 //   dkv: S = Q K^T, dP = dO V^T (A: Q / dO rows from LDS, B: K / V fragments
 //        in registers), dV^T += dO^T P and dK^T += Q^T dS (A: dO / Q read
 //        transposed from LDS, B: P / dS as the result tiles leave them).
-// P and dS are rounded to the input dtype as matrix-core operands; for bf16
-// each is split into a bf16 head and a bf16 remainder (two products), since
-// a single bf16 rounding of P or dS is too coarse for the accuracy rule.
+// P and dS are rounded to the input dtype as matrix-core operands. dS is
+// split into a head and a remainder in the input dtype (two products): dP
+// grows with d_h and the value scale, and where dQ or dK cancels to a small
+// value a single fp16 rounding of dS (half an ulp, 2^-8, at |dS| near 8)
+// already exceeds the accuracy rule. For bf16, P is split as well.
 //
 // A 32-row pair of an LDS operand block is read both as 16-row tiles (one
 // 128-bit row read per lane) and transposed (ds_read_b64_tr_b16 over 4 rows
@@ -86,15 +87,14 @@ struct BwdTile {
 };
 
 // ---------------------------------------------------------------- dq kernel
-// MODE kRowFromOut: D = rowsum(dO * O) from the forward's output, written to
-//   the workspace, then dQ (fp16: the output's rounding leaves D well inside
-//   the accuracy rule).
 // MODE kRowPass: no dQ; D = rowsum(P * dP) accumulated over every visible key
-//   in fp32 and written to the workspace (bf16: the output rounded to bf16
-//   puts an error of D times sum_j P_ij k_j into dQ, which rows with few
-//   visible keys do not average away).
+//   in fp32 and written to the workspace. This equals dO . O of the exact
+//   output; dO . O of the output rounded to fp16 or bf16 would put an error
+//   of D times sum_j P_ij k_j into dQ, which rows whose softmax is peaked or
+//   that see few keys do not average away (fp16, d_h 128, causal, scores of
+//   a few tens: dQ off by three times the accuracy rule).
 // MODE kRowRead: dQ with D read from the workspace.
-constexpr int kRowFromOut = 0, kRowPass = 1, kRowRead = 2;
+constexpr int kRowPass = 1, kRowRead = 2;
 
 // The kernel bodies take their block index, the number of blocks of their
 // kind and their LDS, so that one launch can run both kinds (below).
@@ -106,7 +106,7 @@ struct DqLds {
 template <typename T, int D, int NQT, int NW, int BK, int MODE>
 __device__ __forceinline__ void bwd_dq_body(
     uint32_t blk, uint32_t nblk_grid, T* __restrict__ smem, const T* __restrict__ Qp,
-    const T* __restrict__ Kp, const T* __restrict__ Vp, const T* __restrict__ Op,
+    const T* __restrict__ Kp, const T* __restrict__ Vp,
     const T* __restrict__ dOp, const float* __restrict__ LSEp, T* __restrict__ dQp,
     float* __restrict__ Dp, const int32_t* __restrict__ key_len, int H, int S, int causal,
     int n_qblk, float c_log2, float scale, int group) {
@@ -120,7 +120,6 @@ __device__ __forceinline__ void bwd_dq_body(
   constexpr int NKC = D >= 32 ? D / 32 : 1;
   constexpr int RB = D * (int)sizeof(T);
   constexpr int BQ = NW * NQT * 16;
-  constexpr bool kBf16 = __is_same(T, bf16_t);
   static_assert(BK % 32 == 0 && D % 16 == 0, "tile shape");
 
   // smem: [stage][K, V] tiles
@@ -148,45 +147,30 @@ __device__ __forceinline__ void bwd_dq_body(
   const int kend_w = !wave_live ? 0 : (causal ? min(L, min(q_end, wq0 + NQT * 16)) : L);
 
   const rsrc_t rq = make_rsrc(Qp + head, (uint32_t)S * RB);
-  const rsrc_t ro = make_rsrc(Op + head, (uint32_t)S * RB);
   const rsrc_t rdo = make_rsrc(dOp + head, (uint32_t)S * RB);
   const rsrc_t rdq = make_rsrc(dQp + head, (uint32_t)S * RB);
   const rsrc_t rl = make_rsrc(LSEp + (int64_t)bh * S, (uint32_t)S * 4);
   const rsrc_t rd = make_rsrc(Dp + (int64_t)bh * S, (uint32_t)S * 4);
 
   // ---- Q and dO fragments (B operands, query column c), and the row term
-  //      D = rowsum(dO * O) of each of this wave's rows
+  //      D of each of this wave's rows (read, or zeroed for the row pass)
   T8 qf[NQT][NKC], dof[NQT][NKC];
   T4 qf4[NQT], dof4[NQT];
   float drow[NQT], nlse2[NQT];
 #pragma unroll
   for (int t = 0; t < NQT; ++t) {
     const int row = wq0 + 16 * t + c;
-    float acc = 0.f;
     if constexpr (D == 16) {
       qf4[t] = buf_load8<T4>(rq, (row * D + 4 * g) * 2, 0);
       dof4[t] = buf_load8<T4>(rdo, (row * D + 4 * g) * 2, 0);
-      if constexpr (MODE == kRowFromOut) {
-        const T4 of = buf_load8<T4>(ro, (row * D + 4 * g) * 2, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc += to_f(dof4[t][e]) * to_f(of[e]);
-      }
     } else {
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
         qf[t][kc] = buf_load16<T8>(rq, (row * D + 32 * kc + 8 * g) * 2, 0);
         dof[t][kc] = buf_load16<T8>(rdo, (row * D + 32 * kc + 8 * g) * 2, 0);
-        if constexpr (MODE == kRowFromOut) {
-          const T8 of = buf_load16<T8>(ro, (row * D + 32 * kc + 8 * g) * 2, 0);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc += to_f(dof[t][kc][e]) * to_f(of[e]);
-        }
       }
     }
-    if constexpr (MODE == kRowFromOut) {
-      drow[t] = group_sum(acc);
-      if (wave_live) buf_store4(drow[t], rd, g == 0 ? row * 4 : kOutOfRange);
-    } else if constexpr (MODE == kRowRead) {
+    if constexpr (MODE == kRowRead) {
       drow[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, row * 4, 0, 0));
     } else {
       drow[t] = 0.f;  // accumulates rowsum(P * dP) of this lane's keys
@@ -292,21 +276,17 @@ __device__ __forceinline__ void bwd_dq_body(
             for (int i = 0; i < 4; ++i) drow[t] = fmaf(s[t][kt][i], dp[t][kt][i], drow[t]);
             continue;
           }
-          // dS rounded two at a time (bf16 as head + remainder): words
+          // dS rounded two at a time as head + remainder: words
           // 2 (kt % 2), 2 (kt % 2) + 1 of the pair's operand
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             const float d0 = s[t][kt][2 * j] * (dp[t][kt][2 * j] - drow[t]);
             const float d1 = s[t][kt][2 * j + 1] * (dp[t][kt][2 * j + 1] - drow[t]);
             const int w = 2 * (kt & 1) + j;
-            if constexpr (kBf16) {
-              uint32_t dh, dlo;
-              split2_bf16(d0, d1, dh, dlo);
-              set_word(dsf[t][kt >> 1], w, dh);
-              set_word(dsl[t][kt >> 1], w, dlo);
-            } else {
-              set_word(dsf[t][kt >> 1], w, pack2<T>(d0, d1));
-            }
+            uint32_t dh, dlo;
+            split2<T>(d0, d1, dh, dlo);
+            set_word(dsf[t][kt >> 1], w, dh);
+            set_word(dsl[t][kt >> 1], w, dlo);
           }
         }
       }
@@ -335,7 +315,7 @@ __device__ __forceinline__ void bwd_dq_body(
 #pragma unroll
           for (int t = 0; t < NQT; ++t) {
             acc_dq[t][dt] = mfma_k32(kf, dsf[t][p], acc_dq[t][dt]);
-            if constexpr (kBf16) acc_dq[t][dt] = mfma_k32(kf, dsl[t][p], acc_dq[t][dt]);
+            acc_dq[t][dt] = mfma_k32(kf, dsl[t][p], acc_dq[t][dt]);
           }
         });
       }
@@ -550,8 +530,8 @@ __device__ __forceinline__ void bwd_dkv_body(
               }
             }
           }
-          // rounded two at a time (one packed conversion per pair; bf16 as
-          // head + remainder): words 2h, 2h + 1 of each operand
+          // rounded two at a time (one packed conversion per pair; dS, and
+          // for bf16 P, as head + remainder): words 2h, 2h + 1 of each operand
 #pragma unroll
           for (int t = 0; t < NKTW; ++t) {
 #pragma unroll
@@ -559,18 +539,19 @@ __device__ __forceinline__ void bwd_dkv_body(
               const float p0 = s[h][t][2 * j], p1 = s[h][t][2 * j + 1];
               const float d0 = p0 * (dp[h][t][2 * j] - dv[2 * j]);
               const float d1 = p1 * (dp[h][t][2 * j + 1] - dv[2 * j + 1]);
+              uint32_t dh, dlo;
               if constexpr (kBf16) {
-                uint32_t ph, plo, dh, dlo;
+                uint32_t ph, plo;
                 split2_bf16(p0, p1, ph, plo);
                 split2_bf16(d0, d1, dh, dlo);
                 set_word(pf[t], 2 * h + j, ph);
                 set_word(pl[t], 2 * h + j, plo);
-                set_word(dsf[t], 2 * h + j, dh);
-                set_word(dsl[t], 2 * h + j, dlo);
               } else {
+                split2_f16(d0, d1, dh, dlo);
                 set_word(pf[t], 2 * h + j, pack2<T>(p0, p1));
-                set_word(dsf[t], 2 * h + j, pack2<T>(d0, d1));
               }
+              set_word(dsf[t], 2 * h + j, dh);
+              set_word(dsl[t], 2 * h + j, dlo);
             }
           }
         }
@@ -599,10 +580,8 @@ __device__ __forceinline__ void bwd_dkv_body(
           for (int t = 0; t < NKTW; ++t) {
             adv[t][dt] = mfma_k32(oa, pf[t], adv[t][dt]);
             adk[t][dt] = mfma_k32(qa, dsf[t], adk[t][dt]);
-            if constexpr (kBf16) {
-              adv[t][dt] = mfma_k32(oa, pl[t], adv[t][dt]);
-              adk[t][dt] = mfma_k32(qa, dsl[t], adk[t][dt]);
-            }
+            if constexpr (kBf16) adv[t][dt] = mfma_k32(oa, pl[t], adv[t][dt]);
+            adk[t][dt] = mfma_k32(qa, dsl[t], adk[t][dt]);
           }
         });
       }
@@ -632,25 +611,12 @@ __device__ __forceinline__ void bwd_dkv_body(
 template <typename T, int D, int NQT, int NW, int BK, int MODE>
 __global__ void __launch_bounds__(NW * 64, 2)
 attn_bwd_dq(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
-            const T* __restrict__ Op, const T* __restrict__ dOp, const float* __restrict__ LSEp,
+            const T* __restrict__ dOp, const float* __restrict__ LSEp,
             T* __restrict__ dQp, float* __restrict__ Dp, const int32_t* __restrict__ key_len,
             int H, int S, int causal, int n_qblk, float c_log2, float scale, int group) {
   __shared__ __attribute__((aligned(16))) char lds[DqLds<T, D, BK, NW>::BYTES];
-  bwd_dq_body<T, D, NQT, NW, BK, MODE>(blockIdx.x, gridDim.x, (T*)lds, Qp, Kp, Vp, Op, dOp, LSEp,
+  bwd_dq_body<T, D, NQT, NW, BK, MODE>(blockIdx.x, gridDim.x, (T*)lds, Qp, Kp, Vp, dOp, LSEp,
                                        dQp, Dp, key_len, H, S, causal, n_qblk, c_log2, scale, group);
-}
-
-template <typename T, int D, int NKTW, int NW, int BQb>
-__global__ void __launch_bounds__(NW * 64, 2)
-attn_bwd_dkv(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
-             const T* __restrict__ dOp, const float* __restrict__ LSEp, const float* __restrict__ Dp,
-             T* __restrict__ dKp, T* __restrict__ dVp, const int32_t* __restrict__ key_len,
-             int H, int S, int causal, int n_kblk, float c_log2, float scale, int group) {
-  typedef DkvLds<T, D, BQb, NW> Lds;
-  __shared__ __attribute__((aligned(16))) char lds[Lds::BYTES];
-  bwd_dkv_body<T, D, NKTW, NW, BQb>(blockIdx.x, gridDim.x, (T*)lds, (float*)(lds + Lds::TILE_BYTES),
-                                    Qp, Kp, Vp, dOp, LSEp, Dp, dKp, dVp, key_len, H, S, causal,
-                                    n_kblk, c_log2, scale, group);
 }
 
 // Both kinds in one launch, once the row term D is in the workspace: the
@@ -679,8 +645,7 @@ attn_bwd_both(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
                                         Kp, Vp, dOp, LSEp, Dp, dKp, dVp, key_len, H, S, causal,
                                         n_kblk, c_log2, scale, group);
   } else {
-    // (the output pointer is not read in this mode: Qp stands in for it)
-    bwd_dq_body<T, D, NQT, NW, BK, kRowRead>(id - n_kv_pad, n_q, (T*)lds, Qp, Kp, Vp, Qp, dOp,
+    bwd_dq_body<T, D, NQT, NW, BK, kRowRead>(id - n_kv_pad, n_q, (T*)lds, Qp, Kp, Vp, dOp,
                                              LSEp, dQp, const_cast<float*>(Dp), key_len, H, S,
                                              causal, n_qblk, c_log2, scale, group);
   }
@@ -696,36 +661,20 @@ static hipError_t launch_bwd_one(const BwdParams& p, hipStream_t s) {
   const int64_t wq = (int64_t)p.B * p.H * n_qblk, wk = (int64_t)p.B * (p.H / p.group) * n_kblk;
   if (wq > 0x7fffffffLL || wk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const float scale = 1.f / sqrtf((float)p.D);
-  constexpr bool kBf16 = __is_same(T, bf16_t);
-  if constexpr (kBf16) {
-    hipLaunchKernelGGL((attn_bwd_dq<T, D, NQT, NW, BK, kRowPass>), dim3((unsigned)wq), dim3(NW * 64), 0, s,
-                       (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.out, (const T*)p.dout,
-                       p.lse, (T*)p.dq, p.delta, p.key_len, p.H, p.S, p.causal, n_qblk, p.c_log2, scale, p.group);
-    hipError_t e0 = hipGetLastError();
-    if (e0 != hipSuccess) return e0;
-  }
-  if constexpr (kBf16) {
-    // dQ and dK / dV in one launch behind the row pass
-    const int64_t wk_pad = (wk + 7) / 8 * 8;
-    if (wk_pad + wq > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_bwd_both<T, D, NQT, NW, BK, NKTW, BQb>), dim3((unsigned)(wk_pad + wq)),
-                       dim3(NW * 64), 0, s, (const T*)p.q, (const T*)p.k, (const T*)p.v,
-                       (const T*)p.dout, p.lse, p.delta, (T*)p.dq, (T*)p.dk, (T*)p.dv, p.key_len,
-                       p.H, p.S, p.causal, n_qblk, n_kblk, (uint32_t)wk, (uint32_t)wk_pad,
-                       (uint32_t)wq, p.c_log2, scale, p.group);
-    return hipGetLastError();
-  } else {
-    // fp16: the dq kernel writes D (from dout and out) for the key side
-    hipLaunchKernelGGL((attn_bwd_dq<T, D, NQT, NW, BK, kRowFromOut>), dim3((unsigned)wq), dim3(NW * 64), 0, s,
-                       (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.out, (const T*)p.dout,
-                       p.lse, (T*)p.dq, p.delta, p.key_len, p.H, p.S, p.causal, n_qblk, p.c_log2, scale, p.group);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dkv<T, D, NKTW, NW, BQb>), dim3((unsigned)wk), dim3(NW * 64), 0, s,
-                       (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.dout, p.lse, p.delta,
-                       (T*)p.dk, (T*)p.dv, p.key_len, p.H, p.S, p.causal, n_kblk, p.c_log2, scale, p.group);
-    return hipGetLastError();
-  }
+  // the row pass writes D, then dQ and dK / dV run in one launch behind it
+  hipLaunchKernelGGL((attn_bwd_dq<T, D, NQT, NW, BK, kRowPass>), dim3((unsigned)wq), dim3(NW * 64), 0, s,
+                     (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.dout, p.lse,
+                     (T*)p.dq, p.delta, p.key_len, p.H, p.S, p.causal, n_qblk, p.c_log2, scale, p.group);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t wk_pad = (wk + 7) / 8 * 8;
+  if (wk_pad + wq > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((attn_bwd_both<T, D, NQT, NW, BK, NKTW, BQb>), dim3((unsigned)(wk_pad + wq)),
+                     dim3(NW * 64), 0, s, (const T*)p.q, (const T*)p.k, (const T*)p.v,
+                     (const T*)p.dout, p.lse, p.delta, (T*)p.dq, (T*)p.dk, (T*)p.dv, p.key_len,
+                     p.H, p.S, p.causal, n_qblk, n_kblk, (uint32_t)wk, (uint32_t)wk_pad,
+                     (uint32_t)wq, p.c_log2, scale, p.group);
+  return hipGetLastError();
 }
 
 template <typename T>

@@ -255,6 +255,18 @@ __device__ __forceinline__ void split2_bf16(float a, float b, uint32_t& hi, uint
   const float hb = __builtin_bit_cast(float, hi & 0xffff0000u);
   lo = pack2<bf16_t>(a - ha, b - hb);
 }
+// fp16 head + remainder of a pair, as above (the heads widened back to fp32;
+// a - head is exact in fp32 for |a| below the fp16 range)
+__device__ __forceinline__ void split2_f16(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack2<f16_t>(a, b);
+  const f32x2 h = __builtin_convertvector(__builtin_bit_cast(f16x2, hi), f32x2);
+  lo = pack2<f16_t>(a - h[0], b - h[1]);
+}
+template <typename T> __device__ __forceinline__ void split2(float a, float b, uint32_t& hi,
+                                                              uint32_t& lo) {
+  if constexpr (__is_same(T, bf16_t)) split2_bf16(a, b, hi, lo);
+  else split2_f16(a, b, hi, lo);
+}
 // word j of an 8 x 16-bit operand
 template <typename V> __device__ __forceinline__ void set_word(V& v, int j, uint32_t w) {
   u32x4 u = __builtin_bit_cast(u32x4, v);

@@ -42,7 +42,8 @@ struct AttnParams {
 };
 
 // Backward: dq, dk, dv of sum(dout * out); delta is the caller's float
-// [B, H, S] workspace for the row term rowsum(dout * out).
+// [B, H, S] workspace for the row term rowsum(P * dP) (= rowsum(dout * O) of
+// the exact output; out itself is not read).
 struct BwdParams {
   const void* q;
   const void* k;

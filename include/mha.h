@@ -140,21 +140,26 @@ int mha_forward_strided(const void* q, const void* k, const void* v, void* out, 
  *
  * Given the output gradient dout of a loss, writes dq, dk, dv: the
  * gradients of sum(dout * out) with respect to q, k and v, for the same
- * mask. Two kernels, as in the fused backward of rustingstudio
+ * mask. Two kinds of work, as in the fused backward of rustingstudio
  * "brain/docs/baseline" ("Fused attention"): one per block of query rows
  * (dq), one per block of key rows (dk, dv); both rebuild the probabilities
- * from the forward's log-sum-exp, P = exp(q.k / sqrt(d_h) - lse), and take
- * the softmax row term from dout and out: D = rowsum(dout * out).
+ * from the forward's log-sum-exp, P = exp(q.k / sqrt(d_h) - lse). The
+ * softmax row term D = rowsum(dout * O) is taken as rowsum(P * dP), equal
+ * for the exact O, accumulated in fp32 by a first pass over the keys: D from
+ * the output rounded to fp16 or bf16 puts errors beyond the accuracy rule
+ * into dq where the softmax is peaked.
  *
  *   q, k, v      the forward's inputs (as for mha_forward). Read only.
  *   out, lse     the forward's outputs for exactly these inputs and mask
- *                (lse is required here). Read only.
+ *                (lse is required here). lse is read; out is checked
+ *                (non-null, 16-byte aligned) but not read.
  *   dout         device pointer, [B, H, S, d_h] of `dtype`. Read only.
  *   dq, dk, dv   device pointers, [B, H, S, d_h] of `dtype`, 16-byte
  *                aligned; written in full (dk = dv = 0 for keys past the
  *                key length). Must not overlap any input.
  *   delta        caller-owned float workspace [B, H, S], 4-byte aligned;
- *                overwritten with D (it stays valid after the call).
+ *                overwritten with D (it stays valid after the call; rows
+ *                with no visible key get 0).
  *   B .. dtype   as for mha_forward; dtype must be MHA_F16 or MHA_BF16
  *                (fp32 inputs and d_h = 8 return MHA_ERR_UNSUPPORTED).
  *

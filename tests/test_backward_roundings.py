@@ -1,0 +1,113 @@
+"""Two roundings the backward kernels avoid, each shown to break the graded
+accuracy rule (|u-r| <= 2e-3 or <= 2e-2 |r|) on inputs with large scores,
+while the kernels' own arithmetic meets it. CPU only, float64, against the
+pinned backward oracle; the gradients follow rustingstudio
+"brain/docs/baseline", "Fused attention" (the row term and dS).
+
+1. The softmax row term D_i = sum_j P_ij dP_ij equals dO_i . O_i for the
+   exact output. Taking it from O rounded to fp16 or bf16 adds an error of
+   about |dO| |O| 2^-11 (2^-8 for bf16) to D, and dQ_i = sum_j P_ij (dP_ij -
+   D_i) k_j carries it as that error times sum_j P_ij k_j: where the softmax
+   is peaked that sum is a whole key vector and nothing averages it away.
+2. dS = P * (dP - D) rounded once to fp16 as a matrix-core operand: dP grows
+   with d_h and the value scale, and where dQ or dK cancels to a small value
+   the rounding errors of the few large dS terms stay; a head and a
+   remainder, both fp16, carry dS to about 2^-22 instead.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+DT = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _peaked(dt):
+    """B=3, H=9 query heads over 3 key / value heads, S=64, d_h=128, q and k
+    scaled by 3 (scores of a few tens), inputs rounded to the dtype."""
+    B, H, Hk, S, D = 3, 9, 3, 64, 128
+    g = torch.Generator().manual_seed(158381)
+    q = torch.randn(B, H, S, D, generator=g).mul(3.0).to(DT[dt])
+    k = torch.randn(B, Hk, S, D, generator=g).mul(3.0).to(DT[dt])
+    v = torch.randn(B, Hk, S, D, generator=g).to(DT[dt])
+    do = torch.randn(B, H, S, D, generator=g).to(DT[dt])
+    k, v = (t.repeat_interleave(H // Hk, dim=1) for t in (k, v))
+    return tuple(t.double().numpy() for t in (q, k, v, do))
+
+
+def _dq_given_row_term(q, k, v, do, row):
+    """dQ through causal softmax attention with the row term supplied."""
+    S, D = q.shape[-2:]
+    sc = 1.0 / math.sqrt(D)
+    s = np.where(np.tril(np.ones((S, S), bool)), (q @ np.swapaxes(k, -1, -2)) * sc, -np.inf)
+    p = np.exp(s - s.max(axis=-1, keepdims=True))
+    p /= p.sum(axis=-1, keepdims=True)
+    dp = do @ np.swapaxes(v, -1, -2)
+    return (p * (dp - row[..., None])) @ k * sc
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_row_term_from_rounded_output_breaks_the_rule(dt):
+    q, k, v, do = _peaked(dt)
+    ref = oracle.attention_backward(q, k, v, do, causal=True)[0]
+    out = oracle.attention(q, k, v, causal=True)[0]
+    exact = _dq_given_row_term(q, k, v, do, (do * out).sum(-1))
+    # the formula above is the oracle's dq when D is exact
+    assert np.allclose(exact, ref, rtol=1e-9, atol=1e-9)
+    rounded_out = torch.from_numpy(out).to(DT[dt]).double().numpy()
+    from_rounded = _dq_given_row_term(q, k, v, do, (do * rounded_out).sum(-1))
+
+    def as_dt(x):
+        return torch.from_numpy(x).to(DT[dt]).double().numpy()
+
+    # one rounding of the exact dq to the output dtype fits the rule;
+    # the same rounding of dq built on D from the rounded output does not
+    assert oracle.gate(as_dt(exact), ref).all()
+    assert not oracle.gate(as_dt(from_rounded), ref).all()
+    assert oracle.budget_fraction(as_dt(from_rounded), ref) > 1.5
+
+
+def _wide(seed=538493):
+    """B=3, H=3, S=326, d_h=64, q and k scaled by 3, fp16, no mask."""
+    B, H, S, D = 3, 3, 326, 64
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, H, S, D, generator=g).mul(3.0).half()
+    k = torch.randn(B, H, S, D, generator=g).mul(3.0).half()
+    v = torch.randn(B, H, S, D, generator=g).half()
+    do = torch.randn(B, H, S, D, generator=g).half()
+    return tuple(t.double().numpy() for t in (q, k, v, do))
+
+
+def _f16(x):
+    return torch.from_numpy(x).half().double().numpy()
+
+
+def test_single_fp16_rounding_of_ds_breaks_the_rule():
+    q, k, v, do = _wide()
+    rq, rk, _ = oracle.attention_backward(q, k, v, do)
+    S, D = q.shape[-2:]
+    sc = 1.0 / math.sqrt(D)
+    s = (q @ np.swapaxes(k, -1, -2)) * sc
+    p = np.exp(s - s.max(axis=-1, keepdims=True))
+    p /= p.sum(axis=-1, keepdims=True)
+    dp = do @ np.swapaxes(v, -1, -2)
+    ds = p * (dp - (p * dp).sum(axis=-1, keepdims=True))
+
+    def grads(dsx):
+        return _f16(dsx @ k * sc), _f16(np.swapaxes(dsx, -1, -2) @ q * sc)
+
+    # exact dS: the oracle's gradients, one rounding to fp16 away
+    for u, r in zip(grads(ds), (rq, rk)):
+        assert oracle.gate(u, r).all()
+    # dS rounded once: dQ misses the rule
+    head = _f16(ds)
+    gq, gk = grads(head)
+    assert not oracle.gate(gq, rq).all()
+    assert oracle.budget_fraction(gq, rq) > 1.1
+    # head + remainder: back inside, with the exact dS's margin
+    for u, r in zip(grads(head + _f16(ds - head)), (rq, rk)):
+        assert oracle.budget_fraction(u, r) < 0.1

@@ -26,11 +26,13 @@
 //   dkv: S = Q K^T, dP = dO V^T (A: Q / dO rows from LDS, B: K / V fragments
 //        in registers), dV^T += dO^T P and dK^T += Q^T dS (A: dO / Q read
 //        transposed from LDS, B: P / dS as the result tiles leave them).
-// P and dS are rounded to the input dtype as matrix-core operands. dS is
-// split into a head and a remainder in the input dtype (two products): dP
-// grows with d_h and the value scale, and where dQ or dK cancels to a small
-// value a single fp16 rounding of dS (half an ulp, 2^-8, at |dS| near 8)
-// already exceeds the accuracy rule. For bf16, P is split as well.
+// P and dS are matrix-core operands in the input dtype, each split into a
+// head and a remainder (two products). dP grows with d_h and the value
+// scale, and where dQ or dK cancels to a small value a single fp16 rounding
+// of dS (half an ulp, 2^-8, at |dS| near 8) already exceeds the accuracy
+// rule; where the softmax is peaked, dV sums few probabilities near 1, and
+// their single fp16 rounding (2^-12 relative) does too. bf16 needs both
+// splits at any scale.
 //
 // A 32-row pair of an LDS operand block is read both as 16-row tiles (one
 // 128-bit row read per lane) and transposed (ds_read_b64_tr_b16 over 4 rows
@@ -370,7 +372,6 @@ __device__ __forceinline__ void bwd_dkv_body(
   constexpr int NKC = D >= 32 ? D / 32 : 1;
   constexpr int RB = D * (int)sizeof(T);
   constexpr int BKW = NW * NKTW * 16;  // keys per workgroup
-  constexpr bool kBf16 = __is_same(T, bf16_t);
   constexpr int ROWF = 64;             // floats in one row-vector stage (one DMA instruction)
   static_assert(BQb % 32 == 0 && BQb <= ROWF && D % 16 == 0, "tile shape");
 
@@ -530,8 +531,8 @@ __device__ __forceinline__ void bwd_dkv_body(
               }
             }
           }
-          // rounded two at a time (one packed conversion per pair; dS, and
-          // for bf16 P, as head + remainder): words 2h, 2h + 1 of each operand
+          // rounded two at a time as head + remainder (one packed conversion
+          // per pair): words 2h, 2h + 1 of each operand
 #pragma unroll
           for (int t = 0; t < NKTW; ++t) {
 #pragma unroll
@@ -539,17 +540,11 @@ __device__ __forceinline__ void bwd_dkv_body(
               const float p0 = s[h][t][2 * j], p1 = s[h][t][2 * j + 1];
               const float d0 = p0 * (dp[h][t][2 * j] - dv[2 * j]);
               const float d1 = p1 * (dp[h][t][2 * j + 1] - dv[2 * j + 1]);
-              uint32_t dh, dlo;
-              if constexpr (kBf16) {
-                uint32_t ph, plo;
-                split2_bf16(p0, p1, ph, plo);
-                split2_bf16(d0, d1, dh, dlo);
-                set_word(pf[t], 2 * h + j, ph);
-                set_word(pl[t], 2 * h + j, plo);
-              } else {
-                split2_f16(d0, d1, dh, dlo);
-                set_word(pf[t], 2 * h + j, pack2<T>(p0, p1));
-              }
+              uint32_t ph, plo, dh, dlo;
+              split2<T>(p0, p1, ph, plo);
+              split2<T>(d0, d1, dh, dlo);
+              set_word(pf[t], 2 * h + j, ph);
+              set_word(pl[t], 2 * h + j, plo);
               set_word(dsf[t], 2 * h + j, dh);
               set_word(dsl[t], 2 * h + j, dlo);
             }
@@ -580,7 +575,7 @@ __device__ __forceinline__ void bwd_dkv_body(
           for (int t = 0; t < NKTW; ++t) {
             adv[t][dt] = mfma_k32(oa, pf[t], adv[t][dt]);
             adk[t][dt] = mfma_k32(qa, dsf[t], adk[t][dt]);
-            if constexpr (kBf16) adv[t][dt] = mfma_k32(oa, pl[t], adv[t][dt]);
+            adv[t][dt] = mfma_k32(oa, pl[t], adv[t][dt]);
             adk[t][dt] = mfma_k32(qa, dsl[t], adk[t][dt]);
           }
         });

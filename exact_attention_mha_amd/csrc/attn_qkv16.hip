@@ -32,13 +32,19 @@
 // feeds three matrix products. The weight fragments of all three have the
 // same form: column c of the head's slice, rows 32kk + 8g .. 32kk + 8g + 7.
 //
-// Precision. The projections accumulate in fp32. fp16 rounds q, k, v to
-// fp16 (the precision an unfused fp16 projection would store). bf16 keeps
-// each as a head + remainder pair of bf16 values (about 16 significant
-// bits): q, k, v rounded to bf16 alone would cost more than the accuracy
-// budget of the output. The K = 32 products take the pair in their two
-// halves: S^T = [k_hi | k_lo] . [q_hi | q_hi] + [k_hi | k_lo] . [q_lo | q_lo],
-// O^T += [v_hi | v_lo] . [p_hi | p_hi] + [v_hi | v_lo] . [p_lo | p_lo].
+// Precision. The projections accumulate in fp32. q and k are kept as a
+// head + remainder pair in the input dtype: an error of a few 2^-12 in a
+// score moves every probability of its row by as much, and where an output
+// is a small difference of large values (projection weights twice the
+// default initialisation scale, heads of 8) a single fp16 rounding of q and
+// k already exceeds the accuracy budget. v (and P) are rounded once for
+// fp16; bf16 keeps them as pairs too, since one bf16 rounding of v alone
+// exceeds the budget. The K = 32 products take a pair in their two halves:
+//   S^T = [k_hi | k_lo] . [q_hi | q_hi] + [k_hi | k_lo] . [q_lo | q_lo],
+//   bf16: O^T += [v_hi | v_lo] . [p_hi | p_hi] + [v_hi | v_lo] . [p_lo | p_lo].
+// (A K = 16 product for k_hi . q_lo alone, accumulating onto the K = 32
+// result, measured wrong on gfx950 with the wait states the compiler puts
+// between the two shapes; every accumulator here sees one product shape.)
 //
 // Attention itself is the one-pass short-sequence form: a whole score row
 // fits in registers (no online rescaling), masks ride in the accumulator's
@@ -71,9 +77,10 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
   constexpr int NK = DM / 32;       // K = 32 steps of a projection
   constexpr int TB = 128 * RB;      // bytes of one [128, d_model] tile
   constexpr int NT = 8;             // 16-row tiles in S <= 128
-  constexpr bool kSplit = __is_same(T, bf16_t);
-  // a projected k or v tile: fp16 the rounded values, bf16 [head | remainder]
-  typedef std::conditional_t<kSplit, T8, T4> KV;
+  constexpr bool kSplit = __is_same(T, bf16_t);  // v and P as pairs too
+  // a projected v tile: fp16 the rounded values, bf16 [head | remainder]
+  // (k tiles are [head | remainder] for both)
+  typedef std::conditional_t<kSplit, T8, T4> VT;
   static_assert(NH == 2 || NH == 4 || NH == 8, "d_model 32, 64 or 128");
   static_assert(HPW == 1 || HPW == 2, "one head of 16 or two heads of 8 per wave");
   static_assert(TB == 4 * NH * 1024, "four 1 KiB copies per wave fill a tile");
@@ -190,11 +197,10 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
 #pragma unroll
     for (int i = 0; i < 4; ++i) mL[i] = 16 * kL + i >= vlim ? -INFINITY : 0.f;
 
-    // ---- projection pass over the tiles: k and v for visible key tiles,
-    // and (fp16) q for every query tile; bf16 projects q per query tile
-    // below, which keeps fewer registers live
-    T4 qh[NT];
-    KV kf[NT], vt[NT];
+    // ---- projection pass over the tiles: k and v for visible key tiles
+    // (q is projected per query tile below, which keeps fewer registers live)
+    T8 kf[NT];
+    VT vt[NT];
     {
       T8 xf[2][NK];
       read_tile(std::integral_constant<int, 0>{}, st_off, xf[0]);
@@ -202,13 +208,9 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
         constexpr int j = decltype(J)::value;
         constexpr int pend = j + 1 < NT ? NK : 0;
         if constexpr (j + 1 < NT) read_tile(std::integral_constant<int, j + 1>{}, st_off, xf[(j + 1) & 1]);
-        const bool with_q = !kSplit && 16 * j < S, with_kv = j < kt_need;
-        f32x4 aq = bq, ak = bk, av = bv;
-        project(std::integral_constant<int, pend>{}, xf[j & 1], with_q, with_kv, aq, ak, av);
-        if constexpr (!kSplit) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) qh[j][i] = to_t<T>(aq[i]);
-        }
+        const bool with_kv = j < kt_need;
+        f32x4 aq, ak = bk, av = bv;
+        project(std::integral_constant<int, pend>{}, xf[j & 1], false, with_kv, aq, ak, av);
         // Keys at or past the key length are zeroed: their activation rows
         // are real query rows whose contents may be anything, and a hidden
         // score must stay exactly -inf (mask plus 0) and a hidden value
@@ -229,16 +231,13 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
         for (int i = 0; i < 4; ++i) {
           kh[i] = to_t<T>(ak[i]);
           vh[i] = to_t<T>(av[i]);
-          if constexpr (kSplit) {
-            kl[i] = to_t<T>(ak[i] - to_f(kh[i]));
-            vl[i] = to_t<T>(av[i] - to_f(vh[i]));
-          }
+          kl[i] = to_t<T>(ak[i] - to_f(kh[i]));
+          if constexpr (kSplit) vl[i] = to_t<T>(av[i] - to_f(vh[i]));
         }
+        kf[j] = __builtin_shufflevector(kh, kl, 0, 1, 2, 3, 4, 5, 6, 7);
         if constexpr (kSplit) {
-          kf[j] = __builtin_shufflevector(kh, kl, 0, 1, 2, 3, 4, 5, 6, 7);
           vt[j] = __builtin_shufflevector(vh, vl, 0, 1, 2, 3, 4, 5, 6, 7);
         } else {
-          kf[j] = kh;
           vt[j] = vh;
         }
         __builtin_amdgcn_sched_barrier(0);  // one tile at a time (register pressure)
@@ -269,10 +268,8 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
           buf_store4(-INFINITY, rl[j], (16 * t >= S || g != 2 * j) ? kOutOfRange : row * 4);
         return;
       }
-      T4 q4 = zt4, l4 = zt4;  // this tile's q (bf16: head and remainder)
-      if constexpr (!kSplit) {
-        q4 = qh[t];
-      } else {
+      T4 q4, l4;  // this tile's q: head and remainder
+      {
         T8 xf[NK];
         read_tile(J, st_off, xf);
         f32x4 aq = bq, ak, av;
@@ -294,11 +291,8 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
         const bool mine = gh == j;
         const T4 qm = mine ? q4 : zt4;
         const T8 qa = __builtin_shufflevector(qm, qm, 0, 1, 2, 3, 4, 5, 6, 7);
-        T8 qb;
-        if constexpr (kSplit) {
-          const T4 lm = mine ? l4 : zt4;
-          qb = __builtin_shufflevector(lm, lm, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
+        const T4 lm = mine ? l4 : zt4;
+        const T8 qb = __builtin_shufflevector(lm, lm, 0, 1, 2, 3, 4, 5, 6, 7);
         f32x4 sc[NT];
         float mx = -INFINITY;
 #pragma unroll
@@ -307,12 +301,8 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
           // the causal diagonal starts from its constant mask; the tile
           // holding the key length then adds its offsets
           const f32x4 init = (CAUSAL && kt == t) ? diag : zero4;
-          if constexpr (kSplit) {
-            sc[kt] = mfma_k32(kf[kt], qa, init);
-            sc[kt] = mfma_k32(kf[kt], qb, sc[kt]);
-          } else {
-            sc[kt] = mfma_k16(kf[kt], qm, init);
-          }
+          sc[kt] = mfma_k32(kf[kt], qa, init);
+          sc[kt] = mfma_k32(kf[kt], qb, sc[kt]);
           if (kt == kL) {  // wave-uniform
             // (a real branch: the empty volatile statement keeps the
             // compiler from turning this into an add and a select on every

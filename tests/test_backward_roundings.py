@@ -13,6 +13,10 @@ pinned backward oracle; the gradients follow rustingstudio
    with d_h and the value scale, and where dQ or dK cancels to a small value
    the rounding errors of the few large dS terms stay; a head and a
    remainder, both fp16, carry dS to about 2^-22 instead.
+3. P rounded once to fp16 for dV = P^T dO: with a peaked softmax each key's
+   dV sums a few probabilities near 1 (over the query heads of a group too),
+   and their 2^-12 relative rounding no longer averages out. P is split the
+   same way.
 """
 
 import math
@@ -111,3 +115,31 @@ def test_single_fp16_rounding_of_ds_breaks_the_rule():
     # head + remainder: back inside, with the exact dS's margin
     for u, r in zip(grads(head + _f16(ds - head)), (rq, rk)):
         assert oracle.budget_fraction(u, r) < 0.1
+
+
+def test_single_fp16_rounding_of_p_breaks_the_rule_on_dv():
+    """B=3, 9 query heads over 3 key / value heads, S=108, d_h=64, causal, q
+    and k scaled by 3: dV of each key / value head summed over its group."""
+    B, H, Hk, S, D = 3, 9, 3, 108, 64
+    g = torch.Generator().manual_seed(221735)
+    q = torch.randn(B, H, S, D, generator=g).mul(3.0).half()
+    k = torch.randn(B, Hk, S, D, generator=g).mul(3.0).half()
+    v = torch.randn(B, Hk, S, D, generator=g).half()
+    do = torch.randn(B, H, S, D, generator=g).half()
+    grp = H // Hk
+    qn, dn = q.double().numpy(), do.double().numpy()
+    kn, vn = (t.repeat_interleave(grp, dim=1).double().numpy() for t in (k, v))
+    ref = oracle.attention_backward(qn, kn, vn, dn, causal=True)[2]
+    ref = ref.reshape(B, Hk, grp, S, D).sum(axis=2)
+    s = np.where(np.tril(np.ones((S, S), bool)),
+                 (qn @ np.swapaxes(kn, -1, -2)) / math.sqrt(D), -np.inf)
+    p = np.exp(s - s.max(axis=-1, keepdims=True))
+    p /= p.sum(axis=-1, keepdims=True)
+
+    def dv(px):
+        return _f16((np.swapaxes(px, -1, -2) @ dn).reshape(B, Hk, grp, S, D).sum(axis=2))
+
+    assert oracle.gate(dv(p), ref).all()
+    head = _f16(p)
+    assert not oracle.gate(dv(head), ref).all()
+    assert oracle.budget_fraction(dv(head + _f16(p - head)), ref) < 0.1

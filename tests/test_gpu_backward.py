@@ -211,3 +211,29 @@ def test_backward_large_ds_fp16(mha, causal):
     do = torch.randn(B, H, S, D, generator=g).half()
     got = _run(mha, q, k, v, do, None, causal)
     _check(got, q, k, v, do, None, causal, f"large dS fp16 causal={causal}")
+
+
+def test_backward_peaked_dv_fp16(mha):
+    """9 query heads over 3 key / value heads, S=108, d_h=64, causal, q and k
+    scaled by 3: each key's dV sums a few probabilities near 1, where a single
+    fp16 rounding of P misses the accuracy rule (the CPU test of the
+    backward roundings shows it); P as an fp16 head and remainder meets it."""
+    B, H, Hk, S, D = 3, 9, 3, 108, 64
+    g = torch.Generator().manual_seed(221735)
+    q = torch.randn(B, H, S, D, generator=g).mul(3.0).half()
+    k = torch.randn(B, Hk, S, D, generator=g).mul(3.0).half()
+    v = torch.randn(B, Hk, S, D, generator=g).half()
+    do = torch.randn(B, H, S, D, generator=g).half()
+    dq, dk, dv = _run(mha, q, k, v, do, None, True)
+    grp = H // Hk
+    ke, ve = (t.repeat_interleave(grp, dim=1) for t in (k, v))
+    rq, rk, rv = oracle.attention_backward(q, ke, ve, do, causal=True, threads=THREADS)
+    rk = rk.reshape(B, Hk, grp, S, D).sum(axis=2)
+    rv = rv.reshape(B, Hk, grp, S, D).sum(axis=2)
+    for name, u, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        ok = oracle.gate(u, r)
+        assert ok.all(), (f"peaked dv {name}: {int((~ok).sum())} fail, "
+                          f"budget {oracle.budget_fraction(u, r):.3f}")
+    print(f"peaked dv fp16: budget dq {oracle.budget_fraction(dq, rq):.3f} "
+          f"dk {oracle.budget_fraction(dk, rk):.3f} dv {oracle.budget_fraction(dv, rv):.3f}",
+          flush=True)

@@ -122,7 +122,9 @@ def test_qkv_attention_hidden_rows_stay_local(mha, dt):
 def test_qkv_attention_deterministic_and_matches_unfused(mha):
     """Repeat calls give the same bits; the fused fp16 result agrees with the
     library's own unfused path (projection rounded to fp16, then forward on
-    the head slices) to within one fp16 rounding of the output."""
+    the head slices) to within 2e-3: the fused kernel keeps q and k as fp16
+    pairs, so the two differ by the unfused path's rounding of q and k (about
+    1e-3 at most here in a float64 model)."""
     x, wq, bq, kl = _inputs(64, 128, 8, "f16", seed=5)
     a = _run(mha, x, wq, bq, kl, 8, True)
     b = _run(mha, x, wq, bq, kl, 8, True)
@@ -168,3 +170,16 @@ def test_qkv_attention_heads_of_8_hidden_rows(mha):
     assert torch.equal(po[0, :70], base_o[0, :70]) and torch.equal(po[1, :3], base_o[1, :3])
     assert torch.equal(pl[0, :, :70], base_l[0, :, :70])
     _check(base_o, base_l, x, wq, bq, kl, 16, True, "d8 hidden rows")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("hd", [8, 16])
+def test_qkv_attention_large_weights(mha, hd, dt):
+    """Projection weights at three times the default initialisation scale:
+    q and k rounded once to fp16 would miss the accuracy rule (the CPU test
+    of the QKV roundings shows it); as head + remainder pairs they meet it."""
+    H = 128 // hd
+    x, wq, bq, kl = _inputs(8, 128, H, dt, seed=0, hd=hd)
+    wq = wq * 3.0
+    out, lse = _run(mha, x, wq, bq, kl, H, True)
+    _check(out, lse, x, wq, bq, kl, H, True, f"qkv weights x3 d{hd} {dt}")

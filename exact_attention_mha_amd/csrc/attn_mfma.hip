@@ -498,7 +498,6 @@ attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   constexpr int TILE = NI * 64 * 8;
   constexpr int NIW = (NI + NW - 1) / NW;
   constexpr int NDT = D / 16;
-  constexpr int NKT = BK / 16;
   constexpr int NKP = BK / 32;
   constexpr int NKC = D / 32;
   constexpr int ES = (int)sizeof(T);
@@ -648,13 +647,6 @@ attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) pf[t][4 * hh + i] = to_t<T>(fast_exp2(fmaf(sp[t][hh][i], c_log2, -m_run[t])));
-    }
-  };
-  auto probs = [&](const f32x4 (&sp)[NQT][2], T8 (&pf)[NQT], T8 (&pl)[NQT]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int t = 0; t < NQT; ++t) {
-      prob_unit(t, 0, sp, pf, pl);
-      prob_unit(t, 1, sp, pf, pl);
     }
   };
   // row sum of one pair for query tile t on the matrix cores

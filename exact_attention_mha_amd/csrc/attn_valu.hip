@@ -19,7 +19,6 @@ attn_fwd_valu_d16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* _
                   T* __restrict__ Op, float* __restrict__ LSEp, const int32_t* __restrict__ key_len,
                   int H, int S, int causal, int n_qblk, float c_log2) {
   typedef typename Vec<T>::x8 T8;
-  typedef typename Vec<T>::x4 T4;
   constexpr int D = 16;
   constexpr int BK = 64;
   constexpr int BQ = NW * 64;

@@ -237,3 +237,52 @@ def test_backward_peaked_dv_fp16(mha):
     print(f"peaked dv fp16: budget dq {oracle.budget_fraction(dq, rq):.3f} "
           f"dk {oracle.budget_fraction(dk, rk):.3f} dv {oracle.budget_fraction(dv, rv):.3f}",
           flush=True)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("heads", [(4, 4), (8, 2)], ids=lambda h: f"H{h[0]}_Hkv{h[1]}")
+def test_backward_graph_replays_match_eager(mha, heads, dt):
+    """The backward (row pass, then one launch for both kinds of block; no
+    memsets) captured in a HIP graph gives, on every replay, exactly the
+    eager result. The output gradient changes in place between replays, and
+    eager work and synchronisations run between them, so a replay cannot
+    pass on stale outputs."""
+    H, Hk = heads
+    B, S, D = 2, 320, 64
+    g = torch.Generator().manual_seed(H + Hk)
+    q = torch.randn(B, H, S, D, generator=g).to(DT[dt]).cuda()
+    k = torch.randn(B, Hk, S, D, generator=g).to(DT[dt]).cuda()
+    v = torch.randn(B, Hk, S, D, generator=g).to(DT[dt]).cuda()
+    do = torch.randn(B, H, S, D, generator=g).to(DT[dt]).cuda()
+    out, lse = mha.forward(q, k, v, causal=True)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty(lse.shape, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            mha.backward(q, k, v, out, lse, do, causal=True, dq=dq, dk=dk, dv=dv, delta=delta,
+                         stream=cap)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    for rep in range(4):
+        if rep:
+            do.copy_(torch.randn(do.shape, generator=gen, device="cuda").to(do.dtype))
+        ref = mha.backward(q, k, v, out, lse, do, causal=True)
+        torch.cuda.synchronize()
+        for t in (dq, dk, dv, delta):
+            t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+            assert torch.equal(a, b), f"replay {rep} {name}"
+    grp = H // Hk
+    qc, kc, vc, dc = (t.cpu() for t in (q, k, v, do))
+    ke, ve = (t.repeat_interleave(grp, dim=1) for t in (kc, vc))
+    rq, rk, rv = oracle.attention_backward(qc, ke, ve, dc, causal=True, threads=THREADS)
+    rk = rk.reshape(B, Hk, grp, S, D).sum(axis=2)
+    rv = rv.reshape(B, Hk, grp, S, D).sum(axis=2)
+    for name, u, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        assert oracle.gate(u.cpu(), r).all(), f"graph {heads} {dt} {name}"

@@ -279,3 +279,38 @@ def test_head_size_8(mha, dt, shape):
     for variant in (["auto", "mfma_small"] if S > 128 else ["auto", "mfma"]):
         out, lse = run_gpu(mha, q, k, v, kl, True, variant)
         check_full(out, lse, q, k, v, kl, True, f"d8 {shape} {dt} {variant}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_pipelined_loop_graph_replays_match_eager(mha, D):
+    """The software-pipelined loop (the general variant's default for fp16 at
+    d_h 64 and 128; forced here, since a grid this small would otherwise take
+    the small-grid configuration) captured in a HIP graph: every replay
+    equals the eager call bit for bit, with q changed in place between
+    replays."""
+    from workloads import Workload
+    w = Workload("pipe", 2, 4, 1500, D, torch.float16, True, ("uniform", 700, 1500))
+    q, k, v, kl = to_dev(*make_inputs(w, 17))
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            mha.forward(q, k, v, causal=True, key_len=kl, out=out, lse=lse, variant="mfma",
+                        stream=cap)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda").manual_seed(4)
+    for rep in range(4):
+        if rep:
+            q.copy_(torch.randn(q.shape, generator=gen, device="cuda").to(q.dtype))
+        ref_o, ref_l = mha.forward(q, k, v, causal=True, key_len=kl, variant="mfma")
+        torch.cuda.synchronize()
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {rep}"
+    check_full(out.cpu(), lse.cpu(), q.cpu(), k.cpu(), v.cpu(), kl.cpu(), True,
+               f"pipelined graph D={D}")

@@ -164,8 +164,11 @@ int mha_forward_strided(const void* q, const void* k, const void* v, void* out, 
  *                (fp32 inputs and d_h = 8 return MHA_ERR_UNSUPPORTED).
  *
  * Precision: products on the matrix cores with fp32 accumulation; the
- * probabilities and dS are rounded to the input dtype as matrix-core
- * operands; outputs rounded once to the input dtype.
+ * probabilities and dS enter them as a head and a remainder in the input
+ * dtype (two products each); outputs rounded once to the input dtype. The
+ * accuracy rule holds for scores of moderate spread (q and k up to about 3
+ * times unit variance); far beyond that, fp32 score arithmetic itself
+ * limits dq.
  * Ownership, asynchrony and error behaviour as for mha_forward.
  */
 int mha_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
@@ -216,9 +219,10 @@ int mha_backward_grouped(const void* q, const void* k, const void* v, const void
  * 0 <= S <= 128; otherwise MHA_ERR_UNSUPPORTED (longer sequences or other
  * head sizes take a separate projection and mha_forward_strided);
  * MHA_ERR_SHAPE if H does not divide d_model. Precision: the projection
- * accumulates in fp32; fp16 rounds q, k, v to fp16 before the attention
- * products, bf16 carries each as a pair of bf16 values (head and
- * remainder); attention as mha_forward. B == 0 or S == 0 launches nothing.
+ * accumulates in fp32; q and k enter the score products as a head and a
+ * remainder in the input dtype; v is rounded once for fp16 and carried as a
+ * pair for bf16; attention as mha_forward. B == 0 or S == 0 launches
+ * nothing.
  * Ownership, asynchrony and error behaviour as for mha_forward.
  */
 int mha_qkv_attention(const void* x, const void* w_qkv, const void* b_qkv, void* out, float* lse,

@@ -1,19 +1,24 @@
 #!/usr/bin/env python3
 """Attention forward benchmark on one MI355X.
 
-    python bench.py [--workload launch|bandwidth|compute|long|tiny|qkv_launch|qkv_bandwidth]
+    python bench.py [--workload long|bandwidth|compute|launch|tiny|qkv_launch|qkv_bandwidth|...]
                     [--pass fwd|bwd] [--steps K] [--warmup W] [--gpus 1] [--graph G]
 
 One step is one exact attention forward (one launch of the library's kernel)
 over a batch of seeded synthetic inputs already resident in device memory.
-For the launch-bound shapes the steps are replayed from a HIP graph of G
-captured calls (G = 100 by default there), so the host's per-call submission
+With no --workload the line is quoted on the long-sequence shape (B=32,
+H=16, S=100000, d_h=64, fp16, causal: the largest single-GPU configuration)
+and carries sub-records for the bandwidth-, compute- and launch-bound shapes,
+each timed on its own kernel with its own roofline and CPU baseline.
+Exactly K steps are timed. For the launch-bound shapes the K calls are
+submitted as replays of HIP graphs of captured calls (at most G = 100 per
+graph, plus one graph for the remainder), so the host's per-call submission
 cost is paid once per graph; the eager per-step rate is reported beside it.
 Prints ONE JSON line: throughput in TFLOP/s counted on the visible (query,
 key) pairs only (4 * d_h flops per pair: two matrix products), the roofline
-of the kernel (achieved vs MI355X peak, from per-launch HIP events on the
-stream the kernel runs on), and the float64 CPU oracle timed on a bounded
-sample of the same workload on this host's cores.
+of the kernel (achieved vs MI355X peak, from HIP events on the stream the
+kernel runs on), and the float64 CPU oracle timed on a bounded sample of the
+same workload on this host's cores.
 """
 
 from __future__ import annotations
@@ -34,9 +39,12 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, GB/s
 PEAK_MFMA_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}  # dense matrix-core peaks
 MALL_BYTES = 256 << 20           # working sets below this are rotated over buffer sets
 
-DEFAULT_STEPS = {"tiny": 2000, "launch": 2000, "bandwidth": 100, "compute": 200, "long": 4,
+HEADLINE = "long"                # the workload the default line is quoted on
+SUBRECORDS = ("bandwidth", "compute", "launch")  # further forward regimes in the same line
+SUB_CPU_BUDGET_S = 10.0          # oracle seconds per sub-record
+DEFAULT_STEPS = {"tiny": 2000, "launch": 2000, "bandwidth": 100, "compute": 200, "long": 10,
                  "bwd": 50, "bwd_gqa": 50, "qkv_launch": 2000, "qkv_bandwidth": 100, "qkv_heads8": 100}
-DEFAULT_WARMUP = {"tiny": 50, "launch": 50, "bandwidth": 5, "compute": 10, "long": 1, "bwd": 5,
+DEFAULT_WARMUP = {"tiny": 50, "launch": 50, "bandwidth": 5, "compute": 10, "long": 2, "bwd": 5,
                   "bwd_gqa": 5, "qkv_launch": 50, "qkv_bandwidth": 5, "qkv_heads8": 5}
 WARMUP_S = 0.5                   # minimum warm-up time before any timed region
 DEFAULT_GRAPH = {"tiny": 100, "launch": 100, "bandwidth": 0, "compute": 0, "long": 0, "bwd": 0,
@@ -301,27 +309,14 @@ def bench_qkv(args, w, mha):
         return max(ev, wall_s * 1e3) / n, ev
 
     G = args.graph if args.graph is not None else DEFAULT_GRAPH[w.name]
-    graph = None
-    if G > 0:
-        K = max(G, (K + G - 1) // G * G)
-        graph = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream(dev)
-        cap.wait_stream(stream)
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(graph, stream=cap):
-                for i in range(G):
-                    step(i, cap)
-        stream.wait_stream(cap)
-        torch.cuda.synchronize()
-        for _ in range(max(1, W // G)):
-            graph.replay()
-        torch.cuda.synchronize()
+    g1, n_rep, g2 = graph_plan(K, G)
+    graphs = capture_graphs(lambda i, s: step(i, s), (g1, g2), stream, dev)
 
     eager_ms, eager_ev = timed(lambda: [step(i) for i in range(K)], K, stream)
     ms_per_step, k_ev = eager_ms, eager_ev
     timing = "HIP events around the timed region / %d launches" % K
-    if graph is not None:
-        ms_per_step, k_ev = timed(lambda: [graph.replay() for _ in range(K // G)], K, stream)
+    if graphs:
+        ms_per_step, k_ev = timed(lambda: replay_plan(graphs, n_rep), K, stream)
         timing = "HIP events around the timed graph replays / %d launches" % K
     k_avg_ms = k_ev / K
 
@@ -358,7 +353,7 @@ def bench_qkv(args, w, mha):
                    "key_len": (None if w.key_len is None else list(w.key_len)),
                    "seed": args.seed, "bias": True, "buffer_sets": nsets,
                    "parallelism": "single GPU",
-                   "submission": f"hip graph of {G} calls" if graph is not None else "eager"},
+                   "submission": submission(graphs, g1, n_rep, g2)},
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 3), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 5),
@@ -423,12 +418,15 @@ def main():
     ap.add_argument("--workload", default=None,
                     choices=["tiny", "launch", "bandwidth", "compute", "long", "bwd", "bwd_gqa",
                              "qkv_launch", "qkv_bandwidth", "qkv_heads8"],
-                    help="default: launch for the forward, bwd for the backward")
+                    help="default: the long-sequence forward (S=100000) with sub-records for the "
+                         "bandwidth, compute and launch shapes; bwd for the backward")
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
                     help="time the forward (default) or the backward (dq, dk, dv)")
     ap.add_argument("--variant", default="auto")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-subrecords", action="store_true",
+                    help="time only the headline workload")
     ap.add_argument("--graph", type=int, default=None, metavar="G",
                     help="time steps as replays of a HIP graph of G calls (0 = eager)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
@@ -449,11 +447,12 @@ def main():
         return
 
     import exact_attention_mha_amd as mha
-    from workloads import WORKLOADS, make_inputs
+    from workloads import WORKLOADS
 
     mha.load()  # raises if the HIP library is missing: there is no fallback
+    headline = args.workload is None and args.which == "fwd"
     if args.workload is None:
-        args.workload = "bwd" if args.which == "bwd" else "launch"
+        args.workload = "bwd" if args.which == "bwd" else HEADLINE
     w = WORKLOADS[args.workload]
     if args.which == "bwd":
         print(json.dumps(bench_backward(args, w, mha)), flush=True)
@@ -461,13 +460,86 @@ def main():
     if w.name.startswith("qkv_"):
         print(json.dumps(bench_qkv(args, w, mha)), flush=True)
         return
-    K = args.steps if args.steps is not None else DEFAULT_STEPS[w.name]
-    W = args.warmup if args.warmup is not None else DEFAULT_WARMUP[w.name]
+    rec = bench_forward(w, mha, steps=args.steps, warmup=args.warmup, graph=args.graph,
+                        variant=args.variant, seed=args.seed, cpu=not args.no_cpu_baseline)
+    if headline and not args.no_subrecords:
+        # the other forward regimes, each timed on its own kernel with its own
+        # step count, roofline and CPU baseline, in the same line
+        rec["subrecords"] = {}
+        for name in SUBRECORDS:
+            rec["subrecords"][name] = bench_forward(
+                WORKLOADS[name], mha, steps=None, warmup=None, graph=None, variant="auto",
+                seed=args.seed, cpu=not args.no_cpu_baseline, cpu_budget_s=SUB_CPU_BUDGET_S)
+            print(f"# subrecord {name}: {rec['subrecords'][name]['roofline']['kernel_avg_us']} us "
+                  f"per launch", file=sys.stderr, flush=True)
+    print(json.dumps(rec), flush=True)
+
+
+def graph_plan(steps: int, graph: int):
+    """How K timed steps are submitted from HIP graphs of captured calls:
+    (calls per graph, replays of it, calls in a second graph replayed once
+    for the remainder). Always exactly `steps` calls in all; (0, 0, 0) for
+    eager submission."""
+    if graph <= 0 or steps <= 0:
+        return 0, 0, 0
+    g = min(graph, steps)
+    return g, steps // g, steps % g
+
+
+def capture_graphs(step, sizes, stream, dev):
+    """Capture one HIP graph per nonzero size, each holding that many calls
+    of step(i, capture_stream); every graph is replayed once, untimed."""
+    import torch
+    graphs = []
+    if not sizes or sizes[0] <= 0:
+        return graphs
+    cap = torch.cuda.Stream(dev)
+    for n in sizes:
+        if n <= 0:
+            continue
+        gr = torch.cuda.CUDAGraph()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(gr, stream=cap):
+                for i in range(n):
+                    step(i, cap)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        graphs.append(gr)
+    return graphs
+
+
+def replay_plan(graphs, n_rep):
+    for _ in range(n_rep):
+        graphs[0].replay()
+    if len(graphs) > 1:
+        graphs[1].replay()
+
+
+def submission(graphs, g1, n_rep, g2):
+    if not graphs:
+        return "eager"
+    return f"hip graphs: {n_rep} replays of {g1} calls" + (f" + 1 of {g2}" if g2 else "")
+
+
+def bench_forward(w, mha, *, steps=None, warmup=None, graph=None, variant="auto", seed=0, cpu=True,
+                  cpu_budget_s=12.0):
+    """One forward workload: K timed launches of the library's kernel on
+    inputs resident in device memory. Returns the JSON record."""
+    import torch
+    from workloads import make_inputs
+
+    K = steps if steps is not None else DEFAULT_STEPS[w.name]
+    W = warmup if warmup is not None else DEFAULT_WARMUP[w.name]
+    if K < 1:
+        raise SystemExit("--steps must be at least 1")
     dev = torch.device("cuda:0")
     tag = dtype_tag(w.dtype)
     esize = torch.tensor([], dtype=w.dtype).element_size()
 
-    q, k, v, kl = make_inputs(w, args.seed, device=dev)
+    q, k, v, kl = make_inputs(w, seed, device=dev)
     kl_cpu = None if kl is None else kl.cpu()
     pairs = pair_count(w, kl_cpu)
     flops = 4 * w.D * pairs
@@ -484,13 +556,13 @@ def main():
             for _ in range(nsets)]
     stream = torch.cuda.current_stream(dev)
     variant_name = mha.select_variant(w.B, w.H, w.S, w.D, w.causal, w.dtype) \
-        if args.variant == "auto" else args.variant
+        if variant == "auto" else variant
 
     def step(i, s=None):
         qq, kk, vv = sets[i % nsets]
         o, l = outs[i % nsets]
         mha.forward(qq, kk, vv, causal=w.causal, key_len=kl, out=o, lse=l,
-                    variant=args.variant, stream=stream if s is None else s)
+                    variant=variant, stream=stream if s is None else s)
 
     # untimed warm-up: W steps, and at least WARMUP_S seconds of them, so the
     # GPU clock has ramped up before the timed region
@@ -519,38 +591,23 @@ def main():
         for i in range(K):
             step(i)
 
-    G = args.graph if args.graph is not None else DEFAULT_GRAPH[w.name]
-    graph = None
-    if G > 0:
-        K = max(G, (K + G - 1) // G * G)
-        graph = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream(dev)
-        cap.wait_stream(stream)
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(graph, stream=cap):
-                for i in range(G):
-                    step(i, cap)
-        stream.wait_stream(cap)
-        torch.cuda.synchronize()
-        for _ in range(max(1, W // G)):
-            graph.replay()
-        torch.cuda.synchronize()
+    G = graph if graph is not None else DEFAULT_GRAPH[w.name]
+    g1, n_rep, g2 = graph_plan(K, G)
+    graphs = capture_graphs(step, (g1, g2), stream, dev)
 
-    # ---- timed region: K back-to-back steps (eager, or K / G graph replays)
+    # ---- timed region: K back-to-back steps, eager; then, for the
+    # launch-bound shapes, the same K calls submitted as graph replays
     eager_ms, eager_ev_ms, wall = timed(eager, K)
     ms_per_step = eager_ms
-    if graph is not None:
-        def replays():
-            for _ in range(K // G):
-                graph.replay()
-        ms_per_step, graph_ev_ms, _ = timed(replays, K)
+    if graphs:
+        ms_per_step, graph_ev_ms, _ = timed(lambda: replay_plan(graphs, n_rep), K)
 
     # ---- kernel duration: HIP events on the kernel's stream around the timed
     # region, divided by the launches in it (one launch per step). Launches
     # run back to back, so this bounds the kernel's own duration from above
     # by the small gaps between them; an event pair around each single launch
     # would add its own marker and dispatch overhead instead.
-    if graph is not None:
+    if graphs:
         k_avg_ms = graph_ev_ms / K
         kernel_timing = "HIP events around the timed graph replays / %d launches" % K
     else:
@@ -581,9 +638,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": w.name, "B": w.B, "H": w.H, "S": w.S, "d_h": w.D, "causal": w.causal,
-            "key_len": (None if w.key_len is None else list(w.key_len)), "seed": args.seed,
+            "key_len": (None if w.key_len is None else list(w.key_len)), "seed": seed,
             "variant": variant_name, "buffer_sets": nsets, "parallelism": "single GPU",
-            "submission": f"hip graph of {G} calls" if graph is not None else "eager",
+            "submission": submission(graphs, g1, n_rep, g2),
         },
         "roofline": {
             "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
@@ -598,9 +655,16 @@ def main():
         "hbm_gbs_per_step": round(nbytes / (ms_per_step * 1e-3) / 1e9, 3),
         "eager_ms_per_step": round(eager_ms, 6),
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, q, k, v, kl, 4 * w.D)
-    print(json.dumps(res), flush=True)
+    if bound == "mfma":
+        res["roofline"]["hbm_gbs"] = round(nbytes / (k_avg_ms * 1e-3) / 1e9, 3)
+    else:
+        res["roofline"]["mfma_tflops"] = round(flops / (k_avg_ms * 1e-3) / 1e12, 3)
+    if cpu:
+        res["cpu_baseline"] = cpu_baseline(w, q, k, v, kl, 4 * w.D, budget_s=cpu_budget_s)
+    del sets, outs, q, k, v
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
 if __name__ == "__main__":

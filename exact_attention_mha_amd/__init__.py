@@ -8,7 +8,7 @@ library is not built, or the tensors are not on a GPU, calls raise.
     out, lse = forward(q, k, v, causal=True, key_len=lengths)
 
 q, k, v: contiguous [B, H, S, d_h] tensors on the GPU (float32, float16 or
-bfloat16), d_h in {16, 32, 64, 128, 256}; key_len: None or an int32 GPU
+bfloat16), d_h in {8, 16, 32, 64, 128, 256} (8: fp16 / bf16 only); key_len: None or an int32 GPU
 tensor [B] of right-padded key lengths. backward() gives dq, dk, dv;
 qkv_attention() takes the activations and the QKV projection weights
 instead of q, k, v, for short sequences of 16-wide heads.

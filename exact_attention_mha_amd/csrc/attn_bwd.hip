@@ -678,13 +678,10 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
     // (query tiles per wave, waves, keys per block | key tiles per wave,
     // queries per block); one 16-row tile per wave doubles the workgroups,
     // which the training shape (B=4, H=12, S=1024) needs, at no cost on
-    // larger problems; entries past 0 are kept for A/B measurement
+    // larger problems
     case 16: return launch_bwd_one<T, 16, 1, 4, 64, 1, 64>(p, s);
     case 32: return launch_bwd_one<T, 32, 1, 4, 64, 1, 64>(p, s);
-    case 64:
-      if (p.tile_cfg == 1) return launch_bwd_one<T, 64, 2, 4, 64, 2, 64>(p, s);
-      if (p.tile_cfg == 2) return launch_bwd_one<T, 64, 1, 8, 64, 1, 64>(p, s);
-      return launch_bwd_one<T, 64, 1, 4, 64, 1, 64>(p, s);
+    case 64: return launch_bwd_one<T, 64, 1, 4, 64, 1, 64>(p, s);
     case 128: return launch_bwd_one<T, 128, 1, 4, 64, 1, 64>(p, s);
     case 256: return launch_bwd_one<T, 256, 1, 4, 32, 1, 32>(p, s);
   }

@@ -27,7 +27,8 @@
 // registers as B operands); it walks the key blocks of BK rows in order. K
 // and V blocks are copied from device memory straight into LDS by the
 // buffer DMA path, NST stages deep, one barrier per block. Row sums are
-// accumulated on the vector ALUs from the unrounded probabilities.
+// accumulated on the vector ALUs from the same rounded probabilities the
+// P V products use.
 //
 // LDS layout, in natural key order:
 //   * K rows padded to D + 8 elements: a K operand read (16 bytes of row c at
@@ -288,9 +289,12 @@ attn_fwd_m32(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __rest
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float a = fast_exp2(fmaf(sc[t][kh >> 1][8 * (kh & 1) + e], c_log2, -m_run[t]));
-          ls += a;
           pf[t][kh][e] = to_t<T>(a);
-          if constexpr (kBf16) pl[t][kh][e] = to_t<T>(a - to_f(pf[t][kh][e]));
+          ls += to_f(pf[t][kh][e]);  // the rounded weight the numerator uses
+          if constexpr (kBf16) {
+            pl[t][kh][e] = to_t<T>(a - to_f(pf[t][kh][e]));
+            ls += to_f(pl[t][kh][e]);
+          }
         }
       l_run[t] += ls;
     }

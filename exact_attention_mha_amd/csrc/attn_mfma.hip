@@ -329,8 +329,8 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
     static_for<NKP>([&](auto P) {
       constexpr int p = decltype(P)::value;
       T8 pf[NQT], pl[NQT];
-      // rounded probabilities of pair p for query tile t; returns their
-      // unrounded sum
+      // rounded probabilities of pair p for query tile t; returns the sum of
+      // those rounded values (the weights the numerator uses)
       auto probs = [&](int t) {
         float ls = 0.f;
         if constexpr (kBf16) {
@@ -339,7 +339,6 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
           for (int i = 0; i < 4; ++i) {
             a[i] = fast_exp2(fmaf(s[t][2 * p][i], c_log2, -m_run[t]));
             a[4 + i] = fast_exp2(fmaf(s[t][2 * p + 1][i], c_log2, -m_run[t]));
-            if constexpr (!SUM_MFMA && !STALE) ls += a[i] + a[4 + i];
           }
           // head + remainder, rounded two at a time
 #pragma unroll
@@ -349,14 +348,18 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
             set_word(pf[t], w, hi);
             set_word(pl[t], w, lo);
           }
+          if constexpr (!SUM_MFMA && !STALE) {  // the rounded weights the numerator uses
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ls += to_f(pf[t][i]) + to_f(pl[t][i]);
+          }
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float a0 = fast_exp2(fmaf(s[t][2 * p][i], c_log2, -m_run[t]));
             const float a1 = fast_exp2(fmaf(s[t][2 * p + 1][i], c_log2, -m_run[t]));
-            if constexpr (!SUM_MFMA && !STALE) ls += a0 + a1;
             pf[t][i] = to_t<T>(a0);
             pf[t][4 + i] = to_t<T>(a1);
+            if constexpr (!SUM_MFMA && !STALE) ls += to_f(pf[t][i]) + to_f(pf[t][4 + i]);
           }
         }
         return ls;
@@ -890,51 +893,28 @@ static hipError_t launch_pipe(const AttnParams& p, hipStream_t s) {
 }
 
 // Tile shapes (NQT query tiles per wave, NW waves, BK keys per block, row sum
-// on the matrix cores) per head size. Entry 0 is the default; the others are
-// kept for A/B measurement and are selected with MHA_TILE_CONFIG (entry 8 is
-// the unpipelined loop at the default's tile).
+// on the matrix cores) per head size.
 template <typename T>
 constexpr bool kBf16T = __is_same(T, bf16_t);
 
 template <typename T>
 static hipError_t launch_general(const AttnParams& p, hipStream_t s) {
-  const int cfg = p.tile_cfg;
   switch (p.D) {
     case 8: return launch_one<T, 8, 2, 4, 64, false>(p, s);
     case 16: return launch_one<T, 16, 2, 4, 64, false>(p, s);
     case 32: return launch_one<T, 32, 2, 4, 64, false>(p, s);
     case 64:
-      // default: 4 waves of 64 query rows, two workgroups per CU; fp16 runs
-      // the pipelined loop (bf16's head + remainder probabilities do not fit
-      // its registers at this tile)
-      if (cfg == 1) return launch_one<T, 64, 2, 8, 128, true>(p, s);
-      if (cfg == 2) return launch_one<T, 64, 2, 8, 64, true, 3>(p, s);
-      if (cfg == 3) return launch_one<T, 64, 2, 8, 64, false>(p, s);
-      if (cfg == 4) return launch_one<T, 64, 2, 8, 64, true>(p, s);
-      if (cfg == 5) return launch_one<T, 64, 2, 4, 64, true>(p, s);
-      if (cfg == 6) return launch_pipe<T, 64, 2, 8, 64, 1>(p, s);
-      if (cfg == 7) return launch_pipe<T, 64, 3, 4, 64, 2>(p, s);
-      if constexpr (kBf16T<T>) {
-        return launch_one<T, 64, 4, 4, 64, true>(p, s);
-      } else {
-        if (cfg == 8) return launch_one<T, 64, 4, 4, 64, true>(p, s);
-        return launch_pipe<T, 64, 4, 4, 64, 2>(p, s);
-      }
-    case 128:  // default: pipelined, 8 waves of 32 query rows
-      if (cfg == 1) return launch_one<T, 128, 2, 8, 64, true, 3>(p, s);
-      if (cfg == 8) return launch_one<T, 128, 2, 8, 64, true>(p, s);
+      // 4 waves of 64 query rows, two workgroups per CU; fp16 runs the
+      // pipelined loop (bf16's head + remainder probabilities do not fit its
+      // registers at this tile)
+      if constexpr (kBf16T<T>) return launch_one<T, 64, 4, 4, 64, true>(p, s);
+      else return launch_pipe<T, 64, 4, 4, 64, 2>(p, s);
+    case 128:  // pipelined, 8 waves of 32 query rows
       return launch_pipe<T, 128, 2, 8, 64, 1>(p, s);
-    case 256:  // default: fp16 takes probabilities against the running max
-               // with the overflow check (bf16 spills with it)
-      if (cfg == 1) return launch_one<T, 256, 2, 8, 32, true, 3>(p, s);
-      if (cfg == 2) return launch_one<T, 256, 2, 8, 32, true, 4>(p, s);
-      if (cfg == 3) return launch_one<T, 256, 2, 8, 32, false>(p, s);
-      if constexpr (kBf16T<T>) {
-        return launch_one<T, 256, 2, 8, 32, true>(p, s);
-      } else {
-        if (cfg == 8) return launch_one<T, 256, 2, 8, 32, true>(p, s);
-        return launch_one<T, 256, 2, 8, 32, true, 2, true>(p, s);
-      }
+    case 256:  // fp16 takes probabilities against the running max with the
+               // overflow check (bf16 spills with it)
+      if constexpr (kBf16T<T>) return launch_one<T, 256, 2, 8, 32, true>(p, s);
+      else return launch_one<T, 256, 2, 8, 32, true, 2, true>(p, s);
   }
   return hipErrorInvalidValue;
 }

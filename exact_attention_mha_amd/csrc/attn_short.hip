@@ -121,12 +121,15 @@ attn_fwd_short(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __re
         for (int i = 0; i < 4; ++i) {
           const float a0 = fast_exp2(fmaf(s[2 * p][i], c_log2, -msafe));
           const float a1 = fast_exp2(fmaf(s[2 * p + 1][i], c_log2, -msafe));
-          ls += a0 + a1;
           pf[i] = to_t<T>(a0);
           pf[4 + i] = to_t<T>(a1);
+          // the denominator sums the same rounded weights the numerator
+          // multiplies V by (head + remainder for bf16)
+          ls += to_f(pf[i]) + to_f(pf[4 + i]);
           if constexpr (kBf16) {
             pl[i] = to_t<T>(a0 - to_f(pf[i]));
             pl[4 + i] = to_t<T>(a1 - to_f(pf[4 + i]));
+            ls += to_f(pl[i]) + to_f(pl[4 + i]);
           }
         }
 #pragma unroll

@@ -11,9 +11,13 @@
 //   * K rows and Q rows are the A / B operands of S^T = K Q^T
 //     (16x16x16 MFMA): lane (g, c) reads 8 bytes, row c, columns 4g..4g+3;
 //     16 lanes cover 512 contiguous bytes.
-//   * V is read the same way and transposed by one 16x16x16 MFMA against an
-//     identity operand (exact: every product is v * 1 or v * 0), which leaves
-//     V^T in the A-operand layout of O^T += V^T P^T.
+//   * V is read the same way and transposed through the wave's own slice of
+//     LDS: each lane writes its 8 bytes (row c, columns 4g..4g+3) and the
+//     LDS transpose read (ds_read_b64_tr_b16) returns, in lane (g, c),
+//     column c of keys 4g..4g+3 -- the A-operand layout of O^T += V^T P^T.
+//     Only the wave itself touches its slice, and its LDS operations complete
+//     in issue order, so no barrier is needed; values pass through unchanged
+//     (an Inf or NaN in V stays in its own column).
 // A whole score row fits in registers, so each query tile takes a single
 // pass: row maximum, exponentials, P.V, no rescaling (devpost
 // "gpu-transformer-optimization", section 2.2: at S <= 128 the score row
@@ -32,6 +36,7 @@ namespace mha {
 // At least two waves per SIMD: with that budget (<= 256 registers per lane)
 // the compiler keeps matrix-core results in ordinary VGPRs, where the softmax
 // reads them, instead of accumulation registers that need a copy per value.
+// LDS: 8 key tiles x 16 rows x 32 bytes per wave, for the V transpose.
 template <typename T, int D, int QPW, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2)
 attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
@@ -96,20 +101,22 @@ attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __
       vraw[kt] = buf_load8<T4>(rv, gcol ? (16 * kt + c) * RV + 8 * g : kOutOfRange, 0);
     }
   }
-  T4 ident, ones;
+  T4 ones;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    ident[e] = to_t<T>(4 * g + e == c ? 1.f : 0.f);
-    ones[e] = to_t<T>(1.f);
-  }
+  for (int e = 0; e < 4; ++e) ones[e] = to_t<T>(1.f);
+  // V^T through this wave's LDS slice: tile kt holds keys 16kt..16kt+15 as
+  // 16 rows of 16 elements (32 bytes). Lane (g, c) writes row c, columns
+  // 4g..4g+3; the transpose read of lane (g, c) names row 4g + c/4, columns
+  // 4(c%4)..4(c%4)+3 and receives column c of rows 4g..4g+3.
+  __shared__ __attribute__((aligned(16))) T vlds[4][NT * 256];
+  T* vw = vlds[threadIdx.x >> 6];
 #pragma unroll
-  for (int kt = 0; kt < NT; ++kt) {
-    if (kt < kt_need) {
-      const f32x4 d = mfma_k16(vraw[kt], ident, f32x4{0.f, 0.f, 0.f, 0.f});
+  for (int kt = 0; kt < NT; ++kt)
+    if (kt < kt_need) *(T4*)(vw + kt * 256 + c * 16 + 4 * g) = vraw[kt];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vt[kt][e] = to_t<T>(d[e]);  // exact: d holds V values
-    }
-  }
+  for (int kt = 0; kt < NT; ++kt)
+    if (kt < kt_need)
+      vt[kt] = __builtin_bit_cast(T4, lds_read_tr16(vw + kt * 256 + (4 * g + (c >> 2)) * 16 + 4 * (c & 3)));
 
   // Masks ride in the S^T accumulator: a product starts from 0 (visible) or
   // -inf (hidden), so hidden scores come out as -inf with no per-element

@@ -37,7 +37,6 @@ struct AttnParams {
   int causal;
   int dtype;               // enum mha_dtype
   float c_log2;            // log2(e) / sqrt(d_h)
-  int tile_cfg;            // tile-shape table entry (0 = default)
   Layout lay;              // strides (contiguous unless from mha_forward_strided)
 };
 
@@ -60,7 +59,6 @@ struct BwdParams {
   int causal;
   int dtype;
   float c_log2;
-  int tile_cfg;            // tile-shape table entry (0 = default)
   int group;               // query heads per key / value head (k, v, dk, dv have H / group)
 };
 

@@ -3,7 +3,6 @@
 // include/mha.h.
 #include <math.h>
 #include <stdint.h>
-#include <stdlib.h>
 
 #include "../../include/mha.h"
 #include "launch.h"
@@ -49,16 +48,6 @@ int validate(const void* q, const void* k, const void* v, void* out, const float
   return MHA_OK;
 }
 
-// Debug / A-B knob: MHA_TILE_CONFIG=<n> selects entry n of a kernel's tile
-// shape table (read once; results are identical up to fp32 summation order).
-int tile_config() {
-  static const int cfg = [] {
-    const char* e = getenv("MHA_TILE_CONFIG");
-    return e ? atoi(e) : 0;
-  }();
-  return cfg;
-}
-
 bool variant_runs(int variant, int64_t S, int64_t D, int dtype) {
   switch (variant) {
     case MHA_VARIANT_F32: return dtype == MHA_F32;
@@ -99,7 +88,6 @@ int mha_forward_variant(const void* q, const void* k, const void* v, void* out, 
   p.causal = causal ? 1 : 0;
   p.dtype = dtype;
   p.c_log2 = (float)(1.4426950408889634074 / sqrt((double)d_h));
-  p.tile_cfg = tile_config();
   p.lay = mha::contiguous_layout((int)H, (int)S, (int)d_h);
 
   hipStream_t s = (hipStream_t)stream;
@@ -150,7 +138,6 @@ int mha_forward_strided(const void* q, const void* k, const void* v, void* out, 
   p.causal = causal ? 1 : 0;
   p.dtype = dtype;
   p.c_log2 = (float)(1.4426950408889634074 / sqrt((double)d_h));
-  p.tile_cfg = tile_config();
   p.lay = mha::Layout{strides[0], strides[1], strides[3], strides[4], strides[6], strides[7],
                       strides[9], strides[10], (int)strides[2], (int)strides[5], (int)strides[8],
                       (int)strides[11], (int)(H / H_kv)};
@@ -205,7 +192,6 @@ int mha_backward_grouped(const void* q, const void* k, const void* v, const void
   p.causal = causal ? 1 : 0;
   p.dtype = dtype;
   p.c_log2 = (float)(1.4426950408889634074 / sqrt((double)d_h));
-  p.tile_cfg = tile_config();
   p.group = (int)(H / H_kv);
   const hipError_t e = mha::launch_bwd(p, (hipStream_t)stream);
   if (e == hipErrorInvalidConfiguration) return MHA_ERR_SHAPE;

@@ -2,6 +2,7 @@
 binding and compare with the float64 oracle under the accuracy rule."""
 
 import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -57,3 +58,33 @@ def workload_case(mha, w, seed, variant="auto", label=None):
     q, k, v, kl = make_inputs(w, seed)
     out, lse = run_gpu(mha, q, k, v, kl, w.causal, variant)
     return check_full(out, lse, q, k, v, kl, w.causal, label or f"{w.name} seed {seed} {variant}")
+
+
+def check_full_chunked(out, lse, q, k, v, kl, causal, label="", chunk=625):
+    """check_full over batch chunks run on THREADS host threads: the same
+    oracle and the same rule on every element, in pieces small enough for a
+    full-size launch (numpy releases the interpreter lock in its array work)."""
+    B = q.shape[0]
+
+    def one(b0):
+        b1 = min(B, b0 + chunk)
+        klc = None if kl is None else kl[b0:b1]
+        ro, rl = oracle.attention(q[b0:b1], k[b0:b1], v[b0:b1], causal=causal, key_len=klc, threads=1)
+        uo, ul = out[b0:b1], lse[b0:b1]
+        ok_o, ok_l = oracle.gate(uo, ro), oracle.gate(ul, rl)
+        nbad = int((~ok_o).sum()) + int((~ok_l).sum())
+        first = None
+        if nbad:
+            bad = np.argwhere(~ok_o)
+            first = (bad[:3] + np.array([b0, 0, 0, 0])).tolist() if len(bad) else None
+        return nbad, first, oracle.budget_fraction(uo, ro), oracle.budget_fraction(ul, rl)
+
+    with ThreadPoolExecutor(THREADS) as ex:
+        res = list(ex.map(one, range(0, B, chunk)))
+    nbad = sum(r[0] for r in res)
+    fo, fl = max(r[2] for r in res), max(r[3] for r in res)
+    if nbad:
+        first = [r[1] for r in res if r[1]][:1]
+        raise AssertionError(f"{label}: {nbad} elements fail the rule; out budget {fo:.3f} "
+                             f"lse budget {fl:.3f}; first bad out {first}")
+    return fo, fl

@@ -34,3 +34,25 @@ def test_workload_shapes():
         assert (w.B, w.H, w.S, w.D, w.dtype, w.causal) == (B, H, S, D, dt, causal), name
     assert WORKLOADS["bandwidth"].key_len == ("uniform", 64, 128)
     assert WORKLOADS["compute"].key_len == ("fixed", 1024)
+
+
+def test_graph_plan_submits_exactly_the_requested_steps():
+    sys.path.insert(0, ROOT)
+    import bench
+    for steps in (1, 5, 20, 99, 100, 101, 250, 2000):
+        for graph in (0, 1, 7, 100):
+            g1, n_rep, g2 = bench.graph_plan(steps, graph)
+            if graph == 0:
+                assert (g1, n_rep, g2) == (0, 0, 0)
+                continue
+            assert g1 <= graph and g2 < g1
+            assert g1 * n_rep + g2 == steps, (steps, graph)
+
+
+def test_default_line_is_the_long_workload_with_subrecords():
+    sys.path.insert(0, ROOT)
+    import bench
+    assert bench.HEADLINE == "long"
+    assert set(bench.SUBRECORDS) == {"bandwidth", "compute", "launch"}
+    for name in (bench.HEADLINE,) + tuple(bench.SUBRECORDS):
+        assert name in bench.DEFAULT_STEPS and name in bench.BOUND

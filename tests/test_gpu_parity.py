@@ -12,7 +12,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import check_full, check_rows, run_gpu, to_dev, workload_case, THREADS
+from gpu_helpers import (check_full, check_full_chunked, check_rows, run_gpu, to_dev, workload_case,
+                         THREADS)
 from workloads import WORKLOADS, make_inputs, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -53,27 +54,22 @@ def test_bandwidth_shape_reduced_batch(mha, variant):
 
 
 @pytest.mark.parametrize("chunk", range(5))
-def test_bandwidth_full_size_sampled(mha, chunk):
-    """Full B=10000 launch as timed by the benchmark; 4096 sampled rows per
-    seed against exact oracle rows, plus output-wide properties."""
+def test_bandwidth_full_size_every_element(mha, chunk):
+    """The full B=10000 launch the benchmark times, 25 seeds (5 per chunk),
+    every element of out and lse against the oracle: the pages report this
+    shape failing only in the tail, under a 25-trial stress (devpost
+    "transformerkernel ... Tesla T4", Challenges we ran into)."""
     w = WORKLOADS["bandwidth"]
     fr = []
     for seed in range(5 * chunk, 5 * chunk + 5):
         q, k, v, kl = make_inputs(w, seed)
         out, lse = run_gpu(mha, q, k, v, kl, w.causal)
-        assert torch.isfinite(out).all() and torch.isfinite(lse).all()
-        rows = sample_rows(w.B, w.H, w.S, 4096, seed=seed, tile=16, n_heads=512)
-        fr.append(check_rows(out, lse, q, k, v, kl, w.causal, rows, f"bandwidth seed {seed}"))
-        # row 0 of every head sees key 0 only: out = v_0 (up to one rounding)
+        # row 0 of every head sees key 0 only: out = v_0 exactly
         torch.testing.assert_close(out[:, :, 0].float(), v[:, :, 0].float(), rtol=0, atol=0)
-    _report(f"bandwidth full size chunk {chunk}", fr)
-
-
-def test_bandwidth_full_size_every_element(mha):
-    w = WORKLOADS["bandwidth"]
-    q, k, v, kl = make_inputs(w, 0)
-    out, lse = run_gpu(mha, q, k, v, kl, w.causal)
-    _report("bandwidth full size seed 0 (all elements)", [check_full(out, lse, q, k, v, kl, True, "bw")])
+        fr.append(check_full_chunked(out, lse, q, k, v, kl, w.causal, f"bandwidth seed {seed}"))
+        print(f"bandwidth full size seed {seed}: out budget {fr[-1][0]:.3f} lse budget {fr[-1][1]:.4f}",
+              flush=True)
+    _report(f"bandwidth full size, every element, seeds {5 * chunk}..{5 * chunk + 4}", fr)
 
 
 @pytest.mark.parametrize("chunk", range(5))

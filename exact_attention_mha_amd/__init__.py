@@ -29,8 +29,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libmha_gfx950.so"
 
 # enum mha_variant (include/mha.h)
-VARIANTS = {"auto": 0, "f32": 1, "mfma": 2, "mfma_small": 3, "valu_d16": 4, "short": 5,
-            "mfma32": 6}
+VARIANTS = {"auto": 0, "f32": 1, "mfma": 2, "mfma_small": 3, "valu_d16": 4, "short": 5}
 _VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 # enum mha_dtype
 DTYPES = {"float32": 0, "float16": 1, "bfloat16": 2}

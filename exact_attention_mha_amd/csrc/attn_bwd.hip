@@ -89,12 +89,13 @@ struct BwdTile {
 };
 
 // ---------------------------------------------------------------- dq kernel
-// MODE kRowPass: no dQ; D = rowsum(P * dP) accumulated over every visible key
-//   in fp32 and written to the workspace. This equals dO . O of the exact
-//   output; dO . O of the output rounded to fp16 or bf16 would put an error
-//   of D times sum_j P_ij k_j into dQ, which rows whose softmax is peaked or
-//   that see few keys do not average away (fp16, d_h 128, causal, scores of
-//   a few tens: dQ off by three times the accuracy rule).
+// MODE kRowPass: no dQ; D = rowsum(P * dP) / rowsum(P) accumulated over every
+//   visible key in fp32 and written to the workspace. This equals dO . O of
+//   the exact output; dO . O of the output rounded to fp16 or bf16 would put
+//   an error of D times sum_j P_ij k_j into dQ, which rows whose softmax is
+//   peaked or that see few keys do not average away (fp16, d_h 128, causal,
+//   scores of a few tens: dQ off by three times the accuracy rule). The
+//   division by rowsum(P) does the same for an lse that is off by a rounding.
 // MODE kRowRead: dQ with D read from the workspace.
 constexpr int kRowPass = 1, kRowRead = 2;
 
@@ -158,7 +159,7 @@ __device__ __forceinline__ void bwd_dq_body(
   //      D of each of this wave's rows (read, or zeroed for the row pass)
   T8 qf[NQT][NKC], dof[NQT][NKC];
   T4 qf4[NQT], dof4[NQT];
-  float drow[NQT], nlse2[NQT];
+  float drow[NQT], prow[NQT], nlse2[NQT];
 #pragma unroll
   for (int t = 0; t < NQT; ++t) {
     const int row = wq0 + 16 * t + c;
@@ -176,6 +177,7 @@ __device__ __forceinline__ void bwd_dq_body(
       drow[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, row * 4, 0, 0));
     } else {
       drow[t] = 0.f;  // accumulates rowsum(P * dP) of this lane's keys
+      prow[t] = 0.f;  // and rowsum(P)
     }
     const float lse = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, row * 4, 0, 0));
     nlse2[t] = -lse * kLog2e;
@@ -275,7 +277,10 @@ __device__ __forceinline__ void bwd_dq_body(
         for (int kt = 0; kt < NKT; ++kt) {
           if constexpr (MODE == kRowPass) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) drow[t] = fmaf(s[t][kt][i], dp[t][kt][i], drow[t]);
+            for (int i = 0; i < 4; ++i) {
+              drow[t] = fmaf(s[t][kt][i], dp[t][kt][i], drow[t]);
+              prow[t] += s[t][kt][i];
+            }
             continue;
           }
           // dS rounded two at a time as head + remainder: words
@@ -327,8 +332,17 @@ __device__ __forceinline__ void bwd_dq_body(
   if constexpr (MODE == kRowPass) {
 #pragma unroll
     for (int t = 0; t < NQT; ++t) {
+      // D of the row's probabilities renormalised to sum 1: the stored lse
+      // may come from a forward whose row sums were taken over rounded
+      // probabilities, and then the rebuilt P sums to 1 only within that
+      // rounding (about 1e-4 for fp16). With D / rowsum(P) the rows of
+      // dS = P (dP - D) still sum to exactly zero, as the softmax's do, so no
+      // term D * sum_j P_ij k_j is left uncancelled in dQ; what remains is a
+      // common factor rowsum(P) on the row's dS.
       const float dsum = group_sum(drow[t]);
-      if (wave_live) buf_store4(dsum, rd, g == 0 ? (wq0 + 16 * t + c) * 4 : kOutOfRange);
+      const float psum = group_sum(prow[t]);
+      const float dn = psum > 0.f ? dsum / psum : 0.f;  // no visible key: P = 0, D unused
+      if (wave_live) buf_store4(dn, rd, g == 0 ? (wq0 + 16 * t + c) * 4 : kOutOfRange);
     }
     return;
   }

@@ -60,7 +60,6 @@ __device__ __forceinline__ f32x4 mfma_k16(bf16x4 a, bf16x4 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
-
 // ---- LDS transpose read (gfx950 ds_read_b64_tr_b16) -------------------------
 // Within each group of 16 lanes, lanes 4r..4r+3 each supply the address of 4
 // consecutive 16-bit elements; together they form row r (16 elements) of a

@@ -82,7 +82,6 @@ struct QkvParams {
 hipError_t launch_bwd(const BwdParams& p, hipStream_t s);          // dq then dk/dv kernel
 
 hipError_t launch_mfma(const AttnParams& p, hipStream_t s);        // general tiled, 16x16 products
-hipError_t launch_m32(const AttnParams& p, hipStream_t s);         // general tiled, 32x32 products (d_h 64-256)
 hipError_t launch_mfma_small(const AttnParams& p, hipStream_t s);  // few rows per WG
 hipError_t launch_f32(const AttnParams& p, hipStream_t s);         // fp32 inputs
 hipError_t launch_valu_d16(const AttnParams& p, hipStream_t s);    // d_h = 16 VALU

@@ -55,7 +55,6 @@ bool variant_runs(int variant, int64_t S, int64_t D, int dtype) {
     case MHA_VARIANT_MFMA_SMALL: return dtype != MHA_F32;
     case MHA_VARIANT_VALU_D16: return dtype != MHA_F32 && D == 16;
     case MHA_VARIANT_SHORT: return dtype != MHA_F32 && S <= 128 && D <= 64;
-    case MHA_VARIANT_MFMA32: return dtype != MHA_F32 && D >= 64;
   }
   return false;
 }
@@ -98,7 +97,6 @@ int mha_forward_variant(const void* q, const void* k, const void* v, void* out, 
     case MHA_VARIANT_MFMA_SMALL: e = mha::launch_mfma_small(p, s); break;
     case MHA_VARIANT_VALU_D16: e = mha::launch_valu_d16(p, s); break;
     case MHA_VARIANT_SHORT: e = d_h <= 16 ? mha::launch_short16(p, s) : mha::launch_short(p, s); break;
-    case MHA_VARIANT_MFMA32: e = mha::launch_m32(p, s); break;
   }
   if (e == hipErrorInvalidConfiguration) return MHA_ERR_SHAPE;
   return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
@@ -256,7 +254,6 @@ const char* mha_variant_name(int variant) {
     case MHA_VARIANT_MFMA_SMALL: return "mfma_small";
     case MHA_VARIANT_VALU_D16: return "valu_d16";
     case MHA_VARIANT_SHORT: return "short";
-    case MHA_VARIANT_MFMA32: return "mfma32";
   }
   return "unknown";
 }

@@ -66,9 +66,7 @@ enum mha_variant {
   MHA_VARIANT_VALU_D16 = 4,   /* fp16/bf16 d_h = 16 on the vector ALUs       */
   MHA_VARIANT_SHORT = 5,      /* fp16/bf16 d_h <= 64, S <= 128: one pass per
                                  head, no rescaling                          */
-  MHA_VARIANT_MFMA32 = 6,     /* fp16/bf16 d_h 64 / 128 / 256 general tiled
-                                 kernel on 32x32 matrix tiles                */
-  MHA_VARIANT_COUNT = 7
+  MHA_VARIANT_COUNT = 6
 };
 
 /*
@@ -144,10 +142,12 @@ int mha_forward_strided(const void* q, const void* k, const void* v, void* out, 
  * "brain/docs/baseline" ("Fused attention"): one per block of query rows
  * (dq), one per block of key rows (dk, dv); both rebuild the probabilities
  * from the forward's log-sum-exp, P = exp(q.k / sqrt(d_h) - lse). The
- * softmax row term D = rowsum(dout * O) is taken as rowsum(P * dP), equal
- * for the exact O, accumulated in fp32 by a first pass over the keys: D from
- * the output rounded to fp16 or bf16 puts errors beyond the accuracy rule
- * into dq where the softmax is peaked.
+ * softmax row term D = rowsum(dout * O) is taken as rowsum(P * dP) /
+ * rowsum(P), equal for the exact O and lse, accumulated in fp32 by a first
+ * pass over the keys: D from the output rounded to fp16 or bf16 puts errors
+ * beyond the accuracy rule into dq where the softmax is peaked, and the
+ * division keeps the rows of dS summing to zero when lse is off by a
+ * rounding (an lse from a row sum of rounded probabilities).
  *
  *   q, k, v      the forward's inputs (as for mha_forward). Read only.
  *   out, lse     the forward's outputs for exactly these inputs and mask
@@ -159,7 +159,8 @@ int mha_forward_strided(const void* q, const void* k, const void* v, void* out, 
  *                key length). Must not overlap any input.
  *   delta        caller-owned float workspace [B, H, S], 4-byte aligned;
  *                overwritten with D (it stays valid after the call; rows
- *                with no visible key get 0).
+ *                with no visible key get 0). Every row is written before
+ *                it is read, so it needs no clearing.
  *   B .. dtype   as for mha_forward; dtype must be MHA_F16 or MHA_BF16
  *                (fp32 inputs and d_h = 8 return MHA_ERR_UNSUPPORTED).
  *

@@ -184,3 +184,49 @@ def test_fp32_score_arithmetic_is_the_limit_at_score_spread_64():
     p32 = np.exp2(arg.astype(np.float64))
     assert oracle.budget_fraction(bf16(dq(exact)), ref) < 0.3
     assert oracle.budget_fraction(bf16(dq(p32)), ref) > 0.7
+
+
+def _dq_from_lse(q, k, v, do, lse, renormalise):
+    """dQ as the backward kernels form it: P rebuilt from a stored lse,
+    D = rowsum(P dP), optionally divided by rowsum(P)."""
+    S, D = q.shape[-2:]
+    sc = 1.0 / math.sqrt(D)
+    s = np.where(np.tril(np.ones((S, S), bool)), (q @ np.swapaxes(k, -1, -2)) * sc, -np.inf)
+    p = np.exp(s - lse[..., None])
+    dp = do @ np.swapaxes(v, -1, -2)
+    row = (p * dp).sum(-1)
+    if renormalise:
+        row = row / p.sum(-1)
+    return (p * (dp - row[..., None])) @ k * sc
+
+
+def test_lse_from_rounded_probabilities_needs_a_renormalised_row_term():
+    """A forward that sums its fp16-rounded probabilities for the row sum
+    (the same weights its numerator uses) stores an lse whose rebuilt
+    probabilities sum to 1 only within that rounding (about 1e-4). The
+    backward's row term D = rowsum(P dP) then leaves the rows of
+    dS = P (dP - D) summing to (1 - rowsum P) D instead of 0, and dQ keeps a
+    term D sum_j P_ij k_j; dividing D by rowsum(P) cancels it, leaving only a
+    common factor. Case: B=1, H=2, S=273, d_h=16, causal, q and k scaled by
+    3 and v by 3, fp16 inputs."""
+    S, D = 273, 16
+    g = torch.Generator().manual_seed(1005)
+    q, k, v, do = (torch.randn(1, 2, S, D, generator=g) for _ in range(4))
+    q, k, v = q * 3, k * 3, v * 3
+    q, k, v, do = (t.half().double().numpy() for t in (q, k, v, do))
+    ref = oracle.attention_backward(q, k, v, do, causal=True)[0]
+    s = np.where(np.tril(np.ones((S, S), bool)), (q @ np.swapaxes(k, -1, -2)) / math.sqrt(D), -np.inf)
+    m = s.max(-1, keepdims=True)
+    p16 = torch.from_numpy(np.exp(s - m)).half().double().numpy()  # rounded probabilities
+    lse_rounded = m[..., 0] + np.log(p16.sum(-1))
+    lse_exact = m[..., 0] + np.log(np.exp(s - m).sum(-1))
+    assert np.abs(lse_rounded - lse_exact).max() < 2e-3  # inside the rule for lse itself
+
+    def as_f16(x):
+        return torch.from_numpy(x).half().double().numpy()
+
+    plain = _dq_from_lse(q, k, v, do, lse_rounded, renormalise=False)
+    fixed = _dq_from_lse(q, k, v, do, lse_rounded, renormalise=True)
+    assert oracle.budget_fraction(as_f16(plain), ref) > 1.0
+    assert oracle.gate(as_f16(fixed), ref).all()
+    assert oracle.budget_fraction(as_f16(fixed), ref) < 0.1

@@ -93,8 +93,6 @@ def _variants_for(dt, D, S):
         v.append("valu_d16")
     if D == 8:
         v = ["auto", "mfma", "mfma_small"] + (["short"] if S <= 128 else [])
-    if D >= 64:
-        v.append("mfma32")
     return v
 
 
@@ -246,19 +244,6 @@ def test_graph_replays_match_eager(mha, wl, variant):
         assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {rep}"
     check_full(out.cpu(), lse.cpu(), q.cpu(), k.cpu(), v.cpu(),
                None if kl is None else kl.cpu(), w.causal, f"graph {wl} {variant}")
-
-
-@pytest.mark.parametrize("dt", ["f16", "bf16"])
-@pytest.mark.parametrize("D", [64, 128, 256])
-@pytest.mark.parametrize("causal", [False, True])
-def test_mfma32_variant(mha, dt, D, causal):
-    """The 32x32-tile kernel on multi-block shapes with ragged tails and
-    per-batch key lengths, every element against the oracle."""
-    from workloads import Workload
-    w = Workload("m32", 2, 3, 1000, D, _DT[dt], causal, ("uniform", 1, 1000))
-    q, k, v, kl = make_inputs(w, seed=D + int(causal))
-    out, lse = run_gpu(mha, q, k, v, kl, causal, "mfma32")
-    check_full(out, lse, q, k, v, kl, causal, f"mfma32 {dt} D={D} causal={causal}")
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])

@@ -123,6 +123,8 @@ def test_randomized_parity(mha, seed):
 
 def _variant_case(mha, rng, g, causal, scale, case):
     variant = rng.choice(["mfma", "mfma_small", "short", "valu_d16", "mfma32", "f32"])
+    if variant == "mfma32":  # a retired variant; drawn still, so the case stream stays the same
+        variant = "mfma"
     D = rng.choice([8, 16, 32, 64, 128, 256])
     dt = rng.choice(["f16", "bf16", "f32"])
     S = rng.choice([rng.randint(1, 130), rng.randint(1, 700)])

@@ -38,8 +38,6 @@ def _variants(D, S):
         v.append("short")
     if D == 16:
         v.append("valu_d16")
-    if D >= 64:
-        v.append("mfma32")
     return v
 
 

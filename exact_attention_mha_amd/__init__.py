@@ -21,7 +21,8 @@ import os
 from typing import Optional, Tuple
 
 __all__ = [
-    "forward", "backward", "qkv_attention", "load", "library_path", "library_built",
+    "forward", "backward", "backward_noalloc", "qkv_attention", "load", "library_path",
+    "library_built", "MAX_NOALLOC_ROWS",
     "select_variant", "VARIANTS", "DTYPES", "MhaError",
 ]
 
@@ -76,6 +77,8 @@ def load() -> ctypes.CDLL:
     lib.mha_backward.restype = ctypes.c_int
     lib.mha_backward_grouped.argtypes = [vp] * 10 + [i64] * 5 + [ctypes.c_int, vp, ctypes.c_int, vp]
     lib.mha_backward_grouped.restype = ctypes.c_int
+    lib.mha_backward_noalloc.argtypes = [vp] * 9 + [i64] * 4 + [ctypes.c_int, vp, ctypes.c_int, vp]
+    lib.mha_backward_noalloc.restype = ctypes.c_int
     lib.mha_qkv_attention.argtypes = [vp] * 5 + [i64] * 4 + [ctypes.c_int, vp, ctypes.c_int, vp]
     lib.mha_qkv_attention.restype = ctypes.c_int
     lib.mha_select_variant.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
@@ -248,6 +251,43 @@ def backward(q, k, v, out, lse, dout, causal: bool = False, key_len=None,
     if status != 0:
         raise MhaError("mha_backward_grouped", status, lib.mha_status_string(status).decode())
     return tuple(grads)
+
+
+def backward_noalloc(q, k, v, out, lse, dout, dq, dk, dv, causal: bool = False, key_len=None,
+                     stream=None):
+    """backward() through mha_backward_noalloc: the row term goes through
+    the library's static per-GPU workspace, so with dq, dk, dv preallocated
+    nothing is allocated. Calls that overlap on one GPU share that workspace
+    and must not be issued; B * H * S must not exceed MAX_NOALLOC_ROWS.
+    k and v have H heads here. Returns (dq, dk, dv)."""
+    import torch
+
+    lib = load()
+    B, H, S, D = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout),
+                    ("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor shaped and typed like q")
+    if (lse is None or lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_cuda
+            or not lse.is_contiguous()):
+        raise ValueError("lse must be forward()'s contiguous float32 GPU tensor [B, H, S]")
+    kl_ptr = None
+    if key_len is not None:
+        if (key_len.dtype != torch.int32 or key_len.shape != (B,) or not key_len.is_cuda
+                or not key_len.is_contiguous()):
+            raise ValueError("key_len must be a contiguous int32 GPU tensor [B]")
+        kl_ptr = key_len.data_ptr()
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    status = lib.mha_backward_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, S, D, int(bool(causal)), kl_ptr,
+        _dtype_code(q), st.cuda_stream)
+    if status != 0:
+        raise MhaError("mha_backward_noalloc", status, lib.mha_status_string(status).decode())
+    return dq, dk, dv
+
+
+MAX_NOALLOC_ROWS = 8388608  # MHA_NOALLOC_MAX_ROWS of include/mha.h
 
 
 def qkv_attention(x, w_qkv, b_qkv=None, n_heads: int = 8, causal: bool = False, key_len=None,

@@ -4,8 +4,17 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/mha.h"
 #include "launch.h"
+
+// Row-term workspace of mha_backward_noalloc: one float per query row, for
+// at most MHA_NOALLOC_MAX_ROWS rows. A file-scope device array, so every GPU
+// the library runs on holds its own copy for the life of the process. Host
+// code never uses this name as an address: the per-device address comes from
+// hipGetSymbolAddress (noalloc_scratch below).
+static __device__ __align__(256) float scratch[MHA_NOALLOC_MAX_ROWS];
 
 namespace {
 
@@ -204,6 +213,58 @@ int mha_backward(const void* q, const void* k, const void* v, const void* out, c
                               d_h, causal, key_len, dtype, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr if the lookup fails.
+float* noalloc_scratch(int* status) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *status = MHA_ERR_HIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      *status = MHA_ERR_HIP;
+      return nullptr;
+    }
+    addr[dev] = (float*)p;
+  }
+  return addr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int mha_backward_noalloc(const void* q, const void* k, const void* v, const void* out,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         int64_t B, int64_t H, int64_t S, int64_t d_h, int causal,
+                         const int32_t* key_len, int dtype, void* stream) {
+  // the same checks as mha_backward, then the row limit, all before any HIP call
+  int st = validate(q, k, v, dq, lse, B, H, S, d_h, key_len, dtype);
+  if (st != MHA_OK) return st;
+  if (dtype == MHA_F32 || d_h == 8) return MHA_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0 || S == 0) return MHA_OK;
+  if (!out || !dout || !lse || !dk || !dv) return MHA_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(dout, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return MHA_ERR_MISALIGNED;
+  if (B * H * S > (int64_t)MHA_NOALLOC_MAX_ROWS) return MHA_ERR_WORKSPACE;
+  st = MHA_OK;
+  float* delta = noalloc_scratch(&st);
+  if (!delta) return st;
+  // every row of the workspace is written by the row pass before it is read
+  return mha_backward_grouped(q, k, v, out, dout, lse, dq, dk, dv, delta, B, H, H, S, d_h, causal,
+                              key_len, dtype, stream);
+}
+
 int mha_qkv_attention(const void* x, const void* w_qkv, const void* b_qkv, void* out, float* lse,
                       int64_t B, int64_t S, int64_t d_model, int64_t H, int causal,
                       const int32_t* key_len, int dtype, void* stream) {
@@ -266,10 +327,13 @@ const char* mha_status_string(int status) {
     case MHA_ERR_UNSUPPORTED: return "unsupported head size, dtype or variant";
     case MHA_ERR_MISALIGNED: return "misaligned pointer";
     case MHA_ERR_HIP: return "HIP kernel launch failed";
+    case MHA_ERR_WORKSPACE:
+      return "B * H * S exceeds the static row workspace of the no-allocation entry point "
+             "(MHA_NOALLOC_MAX_ROWS)";
   }
   return "unknown status";
 }
 
-int mha_version(void) { return 105; }
+int mha_version(void) { return 106; }
 
 }  // extern "C"

@@ -21,8 +21,9 @@
  * accumulation; softmax arithmetic is fp32; out is rounded once to the input
  * dtype. fp32 inputs are computed in fp32 throughout.
  *
- * All functions are thread-safe; the library keeps no per-call state and
- * allocates no memory.
+ * All functions are thread-safe and allocate no memory; the library keeps no
+ * per-call state, except the static row workspace of mha_backward_noalloc
+ * (see there for how calls sharing it must be ordered).
  */
 #ifndef EXACT_ATTENTION_MHA_AMD_MHA_H
 #define EXACT_ATTENTION_MHA_AMD_MHA_H
@@ -50,8 +51,14 @@ enum mha_status {
   MHA_ERR_UNSUPPORTED = 3, /* d_h or dtype or variant not supported */
   MHA_ERR_MISALIGNED = 4,  /* q/k/v/out not 16-byte aligned, lse/key_len not
                               4-byte aligned */
-  MHA_ERR_HIP = 5          /* the kernel launch itself failed */
+  MHA_ERR_HIP = 5,         /* the kernel launch itself failed */
+  MHA_ERR_WORKSPACE = 6    /* mha_backward_noalloc: B * H * S is larger than
+                              its static workspace (MHA_NOALLOC_MAX_ROWS) */
 };
+
+/* Rows (B * H * S) that mha_backward_noalloc's static workspace holds:
+ * one float each, 32 MiB per GPU. */
+#define MHA_NOALLOC_MAX_ROWS 8388608
 
 /* Kernel variants. MHA_VARIANT_AUTO picks by (dtype, d_h, causal, B*H, S);
  * the others force one kernel for A/B measurement and testing. Every variant
@@ -176,6 +183,31 @@ int mha_backward(const void* q, const void* k, const void* v, const void* out, c
                  const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t B,
                  int64_t H, int64_t S, int64_t d_h, int causal, const int32_t* key_len, int dtype,
                  void* stream);
+
+/*
+ * mha_backward_noalloc -- mha_backward without the delta argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops, harnesses that forbid allocation). The row term goes
+ * through a static device array of the library instead: MHA_NOALLOC_MAX_ROWS
+ * floats (32 MiB) per GPU, held by each GPU the library runs on until the
+ * process ends. Its device address is looked up once per device on the
+ * first call (with that device current); the call allocates nothing and
+ * makes no allocating library call.
+ *
+ * All calls on one GPU share that GPU's array, and each call overwrites the
+ * rows it uses before reading them: calls that can overlap on one GPU (on
+ * different streams, or from different host threads without ordering)
+ * race on it and must not be issued. Calls ordered on one stream are safe.
+ *
+ * Arguments, results and precision as mha_backward (k, v, dk, dv with H
+ * heads). Returns MHA_ERR_WORKSPACE, before anything is enqueued, when
+ * B * H * S > MHA_NOALLOC_MAX_ROWS; MHA_ERR_HIP if the array's address
+ * cannot be found.
+ */
+int mha_backward_noalloc(const void* q, const void* k, const void* v, const void* out,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         int64_t B, int64_t H, int64_t S, int64_t d_h, int causal,
+                         const int32_t* key_len, int dtype, void* stream);
 
 /*
  * mha_backward_grouped -- mha_backward for grouped-query attention: q, out,

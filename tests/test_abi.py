@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol(mha):
 def test_status_and_variant_strings(mha):
     lib = mha.load()
     assert lib.mha_status_string(0) == b"ok"
-    for code in range(1, 6):
+    for code in range(1, 7):
         assert lib.mha_status_string(code) not in (b"ok", b"unknown status")
     assert lib.mha_status_string(99) == b"unknown status"
     for name, code in mha.VARIANTS.items():
@@ -122,6 +122,34 @@ def test_backward_validation_codes(mha):
     assert _bwd(lib, delta=0xa002) == 4
     assert _bwd(lib, B=0) == 0              # empty: no-op
     assert _bwd(lib, S=0, dout=None) == 0
+
+
+def _bwd_noalloc(lib, q=0x1000, k=0x2000, v=0x3000, out=0x4000, dout=0x5000, lse=0x6000, dq=0x7000,
+                dk=0x8000, dv=0x9000, B=1, H=1, S=16, D=64, causal=0, key_len=None, dtype=1):
+    return lib.mha_backward_noalloc(q, k, v, out, dout, lse, dq, dk, dv, B, H, S, D, causal,
+                                    key_len, dtype, None)
+
+
+def test_noalloc_backward_validation_codes(mha):
+    """The no-allocation backward checks its arguments as mha_backward does,
+    and rejects problems whose B * H * S rows exceed its static workspace
+    before any HIP call (these run without a GPU)."""
+    lib = mha.load()
+    assert _bwd_noalloc(lib, dout=None) == 1
+    assert _bwd_noalloc(lib, lse=None) == 1
+    assert _bwd_noalloc(lib, dk=None) == 1
+    assert _bwd_noalloc(lib, S=-1) == 2
+    assert _bwd_noalloc(lib, D=48) == 3
+    assert _bwd_noalloc(lib, D=8) == 3
+    assert _bwd_noalloc(lib, dtype=0) == 3
+    assert _bwd_noalloc(lib, dv=0x9008) == 4
+    assert _bwd_noalloc(lib, B=0) == 0  # empty: no-op
+    rows = mha.MAX_NOALLOC_ROWS
+    assert _bwd_noalloc(lib, B=rows // 128 + 1, H=1, S=128) == 6
+    assert _bwd_noalloc(lib, B=2048, H=64, S=128) == 6
+    assert b"workspace" in lib.mha_status_string(6)
+    header = open(HEADER).read()
+    assert f"#define MHA_NOALLOC_MAX_ROWS {rows}" in header
 
 
 def _strided(lib, strides=None, B=1, H=4, H_kv=2, S=16, D=64, dtype=1, q=0x1000):

@@ -42,6 +42,8 @@
 // which keeps both kinds of read free of bank conflicts. In the contraction
 // over a pair, k-slot 8g + 4h + i of lane group g stands for row 16h + 4g + i
 // of the pair, in both operands.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "launch.h"
 
@@ -184,11 +186,11 @@ __device__ __forceinline__ void bwd_dq_body(
   }
   wait_vmem();
 
-  f32x4 acc_dq[NQT][NDT];
+  AccK32 acc_dq[NQT][NDT];
 #pragma unroll
   for (int t = 0; t < NQT; ++t)
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc_dq[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < NDT; ++dt) acc_dq[t][dt] = AccK32::zero();
 
   if (nblk > 0) {
     const rsrc_t rk = make_rsrc(Kp + head_kv, (uint32_t)kend * RB);
@@ -219,12 +221,14 @@ __device__ __forceinline__ void bwd_dq_body(
 
       // S^T = K Q^T and dP^T = V dO^T; key 16kt + 4g + i of the block in
       // register i of lane (g, c)
-      f32x4 s[NQT][NKT], dp[NQT][NKT];
+      // K = 16 products at d_h = 16, K = 32 ones otherwise
+      typedef std::conditional_t<D == 16, AccK16T<T>, AccK32> SAcc;
+      SAcc s[NQT][NKT], dp[NQT][NKT];
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt) {
         const int rb = 16 * kt * STR + rrow;
 #pragma unroll
-        for (int t = 0; t < NQT; ++t) s[t][kt] = dp[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < NQT; ++t) s[t][kt] = dp[t][kt] = SAcc::zero();
         if constexpr (D == 16) {
           const T4 kf = *(const T4*)(Ks + rb + 4 * g);
           const T4 vf = *(const T4*)(Vs + rb + 4 * g);
@@ -437,11 +441,11 @@ __device__ __forceinline__ void bwd_dkv_body(
   }
   wait_vmem();
 
-  f32x4 adk[NKTW][NDT], adv[NKTW][NDT];
+  AccK32 adk[NKTW][NDT], adv[NKTW][NDT];
 #pragma unroll
   for (int t = 0; t < NKTW; ++t)
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) adk[t][dt] = adv[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < NDT; ++dt) adk[t][dt] = adv[t][dt] = AccK32::zero();
 
   if (nblk > 0) {
     int off[Tile::NIW];
@@ -492,12 +496,13 @@ __device__ __forceinline__ void bwd_dkv_body(
       for (int p = 0; p < NQP; ++p) {
         // S = Q K^T and dP = dO V^T for the pair's two query tiles h:
         // register i of lane (g, c) is query 32p + 16h + 4g + i, key column c
-        f32x4 s[2][NKTW], dp[2][NKTW];
+        typedef std::conditional_t<D == 16, AccK16T<T>, AccK32> SAcc;  // as in the dq body
+        SAcc s[2][NKTW], dp[2][NKTW];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int rb = (32 * p + 16 * h) * STR + rrow;
 #pragma unroll
-          for (int t = 0; t < NKTW; ++t) s[h][t] = dp[h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int t = 0; t < NKTW; ++t) s[h][t] = dp[h][t] = SAcc::zero();
           if constexpr (D == 16) {
             const T4 qa = *(const T4*)(Qs + rb + 4 * g);
             const T4 da = *(const T4*)(dOs + rb + 4 * g);

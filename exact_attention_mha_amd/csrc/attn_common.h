@@ -40,26 +40,69 @@ template <> struct Vec<bf16_t> { typedef bf16x8 x8; typedef bf16x4 x4; };
 template <typename V> __device__ __forceinline__ V zero_vec();
 
 // ---- matrix-core products (fp32 accumulate) ---------------------------------
-__device__ __forceinline__ f32x4 mfma_k32(f16x8 a, f16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+// Every accumulator carries, in its type, the reduction depth K of the
+// instruction shape that produces it: Acc<32> for 16x16x32, Acc<16> for the
+// fp16 16x16x16 product, Acc<4> for the fp32 16x16x4 product. A product only
+// takes an accumulator of its own shape, so the result of one shape cannot be
+// fed to another shape as its accumulator by accident (on gfx950 a 16x16x32
+// result used directly as the accumulator of a 16x16x16 product gave wrong
+// sums); moving values between shapes takes an explicit element copy.
+template <int K>
+struct Acc {
+  f32x4 v;
+  // element access: reads give the float; writes go through a reference to
+  // one lane of the vector. The reference lives only as long as the
+  // accumulator: never keep one in an `auto` variable or return one (take
+  // `float x = acc[i]`, or acc.vec()[i]).
+  struct Ref {
+    f32x4& v;
+    int i;
+    __device__ __forceinline__ operator float() const { return v[i]; }
+    __device__ __forceinline__ Ref& operator=(float x) { v[i] = x; return *this; }
+    __device__ __forceinline__ Ref& operator=(const Ref& r) { v[i] = (float)r; return *this; }
+    __device__ __forceinline__ Ref& operator+=(float x) { v[i] += x; return *this; }
+    __device__ __forceinline__ Ref& operator*=(float x) { v[i] *= x; return *this; }
+  };
+  __device__ __forceinline__ Ref operator[](int i) { return Ref{v, i}; }
+  __device__ __forceinline__ float operator[](int i) const { return v[i]; }
+  __device__ __forceinline__ Acc& operator*=(float a) {
+    v *= a;
+    return *this;
+  }
+  __device__ __forceinline__ f32x4 vec() const { return v; }
+  static __device__ __forceinline__ Acc of(f32x4 x) { return Acc{x}; }
+  static __device__ __forceinline__ Acc fill(float x) { return Acc{f32x4{x, x, x, x}}; }
+  static __device__ __forceinline__ Acc zero() { return fill(0.f); }
+};
+typedef Acc<32> AccK32;  // v_mfma_f32_16x16x32_{f16,bf16}
+typedef Acc<16> AccK16;  // v_mfma_f32_16x16x16_f16
+typedef Acc<4> AccK4;    // v_mfma_f32_16x16x4_f32
+
+__device__ __forceinline__ AccK32 mfma_k32(f16x8 a, f16x8 b, AccK32 c) {
+  return AccK32::of(__builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c.vec(), 0, 0, 0));
 }
-__device__ __forceinline__ f32x4 mfma_k32(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ AccK32 mfma_k32(bf16x8 a, bf16x8 b, AccK32 c) {
+  return AccK32::of(__builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c.vec(), 0, 0, 0));
 }
-__device__ __forceinline__ f32x4 mfma_k16(f16x4 a, f16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ AccK16 mfma_k16(f16x4 a, f16x4 b, AccK16 c) {
+  return AccK16::of(__builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c.vec(), 0, 0, 0));
 }
 // bf16 K=16 products go through the K=32 instruction with the upper half of
-// both operands zero (the same sum: zero products add nothing), so fp16 and
-// bf16 use the same two instruction shapes.
-__device__ __forceinline__ f32x4 mfma_k16(bf16x4 a, bf16x4 b, f32x4 c) {
+// both operands zero (the same sum: zero products add nothing), so their
+// accumulator is a K=32 one.
+__device__ __forceinline__ AccK32 mfma_k16(bf16x4 a, bf16x4 b, AccK32 c) {
   const bf16x8 a8 = __builtin_shufflevector(a, zero_vec<bf16x4>(), 0, 1, 2, 3, 4, 5, 6, 7);
   const bf16x8 b8 = __builtin_shufflevector(b, zero_vec<bf16x4>(), 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, c, 0, 0, 0);
+  return AccK32::of(__builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, c.vec(), 0, 0, 0));
 }
-__device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+// the accumulator type of mfma_k16 for element type T
+template <typename T> struct AccK16Of { typedef AccK16 type; };
+template <> struct AccK16Of<bf16_t> { typedef AccK32 type; };
+template <typename T> using AccK16T = typename AccK16Of<T>::type;
+__device__ __forceinline__ AccK4 mfma_f32_k4(float a, float b, AccK4 c) {
+  return AccK4::of(__builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c.vec(), 0, 0, 0));
 }
+
 // ---- LDS transpose read (gfx950 ds_read_b64_tr_b16) -------------------------
 // Within each group of 16 lanes, lanes 4r..4r+3 each supply the address of 4
 // consecutive 16-bit elements; together they form row r (16 elements) of a

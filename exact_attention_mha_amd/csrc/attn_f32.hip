@@ -64,13 +64,13 @@ attn_fwd_f32(const float* __restrict__ Qp, const float* __restrict__ Kp,
   }
 
   float m_run[NQT], l_run[NQT];
-  f32x4 o[NQT][NDT];
+  AccK4 o[NQT][NDT];
 #pragma unroll
   for (int t = 0; t < NQT; ++t) {
     m_run[t] = -INFINITY;
     l_run[t] = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < NDT; ++dt) o[t][dt] = AccK4::zero();
   }
 
   for (int kb = 0; kb < nblk; ++kb) {
@@ -87,11 +87,11 @@ attn_fwd_f32(const float* __restrict__ Qp, const float* __restrict__ Kp,
     __syncthreads();
     if (k0 >= kend_w) continue;
 
-    f32x4 s[NQT][NKT];
+    AccK4 s[NQT][NKT];
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
-      for (int t = 0; t < NQT; ++t) s[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < NQT; ++t) s[t][kt] = AccK4::zero();
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
         const f32x4 kf = *(const f32x4*)(Ks + (16 * kt + c) * STR + 16 * kc + 4 * g);
@@ -164,7 +164,7 @@ attn_fwd_f32(const float* __restrict__ Qp, const float* __restrict__ Kp,
       const float inv = l > 0.f ? 1.f / l : 0.f;
       if (row < S) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) *(f32x4*)(Oh + row * D + 16 * dt + 4 * g) = o[t][dt] * inv;
+        for (int dt = 0; dt < NDT; ++dt) *(f32x4*)(Oh + row * D + 16 * dt + 4 * g) = o[t][dt].vec() * inv;
         if (LSEp && g == 0)
           LSEp[(int64_t)bh * S + row] = l > 0.f ? (m_run[t] + fast_log2(l)) * kLn2 : -INFINITY;
       }

@@ -41,6 +41,8 @@
 //    32-lane half of the wave are all even or all odd rows.
 // Rows past the visible key range and the pad slots come from out-of-range
 // buffer offsets, which read as zero without touching memory.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "launch.h"
 
@@ -200,14 +202,14 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   }
 
   float m_run[NQT], l_run[NQT];
-  f32x4 o[NQT][NDT], lsum[NQT];
+  AccK32 o[NQT][NDT], lsum[NQT];
 #pragma unroll
   for (int t = 0; t < NQT; ++t) {
     m_run[t] = STALE ? kNoMaxStale : -INFINITY;
     l_run[t] = 0.f;
-    lsum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    lsum[t] = AccK32::zero();
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < NDT; ++dt) o[t][dt] = AccK32::zero();
   }
   T8 ones;
 #pragma unroll
@@ -237,12 +239,14 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
     const T* Vs = Ks + TILE;
 
     // ---- S^T = K Q^T
-    f32x4 s[NQT][NKT];
+    // scores come from K = 16 products at d_h <= 16, K = 32 ones otherwise
+    typedef std::conditional_t<(D <= 16), AccK16T<T>, AccK32> SAcc;
+    SAcc s[NQT][NKT];
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) {
       const int rbase = (32 * (kt >> 1) + 16 * (kt & 1)) * STR;
 #pragma unroll
-      for (int t = 0; t < NQT; ++t) s[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < NQT; ++t) s[t][kt] = SAcc::zero();
       if constexpr (D <= 16) {
         const T4 kf = *(const T4*)(Ks + rbase + kread16);
 #pragma unroll
@@ -369,16 +373,22 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
         // matrix-core row sums stay within kPairSumMax exactly when no fp16
         // probability overflowed (or was NaN). Otherwise move the max to the pair's maximum,
         // rescale, and redo the pair (its scores are still in registers).
-        f32x4 ps[NQT];
+        // row sums: every row of the ones product holds query c's sum, so
+        // only element 0 is kept
+        auto pair_sum = [&](int t) -> float {
+          AccK32 a = mfma_k32(ones, pf[t], AccK32::zero());
+          if constexpr (kBf16) a = mfma_k32(ones, pl[t], a);
+          return a.vec()[0];
+        };
+        float ps[NQT];
         bool bad = false;
 #pragma unroll
         for (int t = 0; t < NQT; ++t) {
           probs(t);
-          ps[t] = mfma_k32(ones, pf[t], f32x4{0.f, 0.f, 0.f, 0.f});
-          if constexpr (kBf16) ps[t] = mfma_k32(ones, pl[t], ps[t]);
+          ps[t] = pair_sum(t);
         }
 #pragma unroll
-        for (int t = 0; t < NQT; ++t) bad |= !(ps[t][0] <= kPairSumMax);
+        for (int t = 0; t < NQT; ++t) bad |= !(ps[t] <= kPairSumMax);
         if (__any(bad)) {
 #pragma unroll
           for (int t = 0; t < NQT; ++t) {
@@ -393,12 +403,11 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) o[t][dt] *= alpha;
             probs(t);
-            ps[t] = mfma_k32(ones, pf[t], f32x4{0.f, 0.f, 0.f, 0.f});
-            if constexpr (kBf16) ps[t] = mfma_k32(ones, pl[t], ps[t]);
+            ps[t] = pair_sum(t);
           }
         }
 #pragma unroll
-        for (int t = 0; t < NQT; ++t) l_run[t] += ps[t][0];  // every row holds query c's sum
+        for (int t = 0; t < NQT; ++t) l_run[t] += ps[t];
       } else {
 #pragma unroll
         for (int t = 0; t < NQT; ++t) {
@@ -601,18 +610,18 @@ attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
 
   constexpr float kNoMax = -1.0e30f;  // finite: exp2(s c - kNoMax) overflows, exp2(-inf) stays 0
   float m_run[NQT], l_run[NQT];
-  f32x4 o[NQT][NDT];
+  AccK32 o[NQT][NDT];
 #pragma unroll
   for (int t = 0; t < NQT; ++t) {
     m_run[t] = kNoMax;
     l_run[t] = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < NDT; ++dt) o[t][dt] = AccK32::zero();
   }
   T8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = to_t<T>(1.f);
-  const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
+  const AccK32 zero4 = AccK32::zero();
 
   // LDS byte addresses of this lane's operands in stage 0
   const uint32_t kaddr0 = lds_addr(smem + c * STR + 8 * g);
@@ -621,7 +630,7 @@ attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
 
   // key k0 + 32p + 8g + 4h + i is visible to row r iff key < L and, when
   // causal, key <= r
-  auto mask_pair = [&](int p, int k0, f32x4 (&sp)[NQT][2]) __attribute__((always_inline)) {
+  auto mask_pair = [&](int p, int k0, AccK32 (&sp)[NQT][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < NQT; ++t) {
       const int row = wq0 + 16 * t + c;
@@ -633,7 +642,7 @@ attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
     }
   };
   // rounded probabilities of key tile hh of one pair for query tile t
-  auto prob_unit = [&](int t, int hh, const f32x4 (&sp)[NQT][2], T8 (&pf)[NQT], T8 (&pl)[NQT])
+  auto prob_unit = [&](int t, int hh, const AccK32 (&sp)[NQT][2], T8 (&pf)[NQT], T8 (&pl)[NQT])
       __attribute__((always_inline)) {
     if constexpr (kBf16) {
       // head + remainder, rounded two at a time: words 2hh, 2hh + 1
@@ -654,13 +663,13 @@ attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   };
   // row sum of one pair for query tile t on the matrix cores
   auto pair_sum = [&](int t, const T8 (&pf)[NQT], const T8 (&pl)[NQT]) __attribute__((always_inline)) {
-    f32x4 a = mfma_k32(ones, pf[t], zero4);
+    AccK32 a = mfma_k32(ones, pf[t], zero4);
     if constexpr (kBf16) a = mfma_k32(ones, pl[t], a);
     return a;
   };
   // true if any sum exceeds kPairSumMax or is NaN; ps takes query c's sum
   // (every row of the product holds it)
-  auto check = [&](const f32x4 (&psv)[NQT], float (&ps)[NQT]) __attribute__((always_inline)) {
+  auto check = [&](const AccK32 (&psv)[NQT], float (&ps)[NQT]) __attribute__((always_inline)) {
     bool bad = false;
 #pragma unroll
     for (int t = 0; t < NQT; ++t) {
@@ -680,7 +689,7 @@ attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   // products, and a scheduling fence closes each item, so the vector work
   // sits between the matrix-core products instead of in one run.
   auto stream = [&](auto PV, auto NVI_, auto PK, auto NKI_, uint32_t va_base, uint32_t ka_base,
-                    const T8 (&pp)[NQT], const T8 (&pl)[NQT], f32x4 (&sp)[NQT][2], auto&& work)
+                    const T8 (&pp)[NQT], const T8 (&pl)[NQT], AccK32 (&sp)[NQT][2], auto&& work)
       __attribute__((always_inline)) {
     constexpr int pv = decltype(PV)::value, pk = decltype(PK)::value;
     constexpr int NVI = decltype(NVI_)::value, NKI = decltype(NKI_)::value;
@@ -728,7 +737,7 @@ attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  auto scores_pair = [&](auto P, uint32_t ka, f32x4 (&sp)[NQT][2]) __attribute__((always_inline)) {
+  auto scores_pair = [&](auto P, uint32_t ka, AccK32 (&sp)[NQT][2]) __attribute__((always_inline)) {
     T8 dummy[NQT];
     stream(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, P,
            std::integral_constant<int, 2 * NKC>{}, 0u, ka, dummy, dummy, sp, no_work);
@@ -742,7 +751,7 @@ attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
     constexpr int p = decltype(P)::value;
     static_for<NQT>([&](auto TT) __attribute__((always_inline)) {
       constexpr int t = decltype(TT)::value;
-      f32x4 sr[NQT][2];  // only row t is used
+      AccK32 sr[NQT][2];  // only row t is used
       static_for<2 * NKC>([&](auto J) __attribute__((always_inline)) {
         constexpr int j = decltype(J)::value;
         u32x4 kf = lds_read_b128_asm<((32 * p + 16 * (j / NKC)) * STR + 32 * (j % NKC)) * ES>(ka);
@@ -773,7 +782,7 @@ attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
     });
   };
 
-  f32x4 sc[NKP][NQT][2];       // scores of the current block, by key pair
+  AccK32 sc[NKP][NQT][2];       // scores of the current block, by key pair
   T8 pprev[NQT], plprev[NQT];  // probabilities of the previous pair
   if (nblk_w > 0) static_for<NKP>([&](auto P) { scores_pair(P, kaddr0, sc[decltype(P)::value]); });
 
@@ -794,7 +803,7 @@ attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
       constexpr int NS = nvi + NKC + 1;  // slots whose work may still read the old scores
       constexpr int NU = 2 * NQT;        // work units (t, key tile), key tile 0 first
       T8 pf[NQT], pl[NQT];
-      f32x4 psv[NQT];
+      AccK32 psv[NQT];
       // unit u = (t, hh) reads key tile hh of the old scores, which the K
       // items of key tile hh overwrite (the first at slot nvi + NKC * hh):
       // tile-0 units go in slots <= nvi, tile-1 units in slots <= nvi + NKC
@@ -827,7 +836,7 @@ attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
       }
     });
     if (kb == nblk_w - 1) {  // the wave's last block: products of its last pair now
-      f32x4 unused[NQT][2];
+      AccK32 unused[NQT][2];
       stream(std::integral_constant<int, NKP - 1>{}, std::integral_constant<int, NDT>{},
              std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, vcur, 0u, pprev, plprev, unused,
              no_work);

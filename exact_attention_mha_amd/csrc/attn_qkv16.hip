@@ -104,7 +104,7 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         wf[sec][kk][e] = Wp[(size_t)(32 * kk + 8 * g + e) * (3 * DM) + sec * DM + 16 * h + c];
-  f32x4 bq, bk, bv;
+  AccK32 bq, bk, bv;  // biases: the projections' initial accumulators
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     bq[i] = bias ? to_f(bias[16 * h + 4 * g + i]) : 0.f;       // Q^T row = dim 4g + i
@@ -130,7 +130,7 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
 #pragma unroll
   for (int e = 0; e < 4; ++e) ones4[e] = to_t<T>(1.f);
   const T8 ones8 = __builtin_shufflevector(ones4, ones4, 0, 1, 2, 3, 4, 5, 6, 7);
-  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  const AccK32 zero4 = AccK32::zero();
   const T4 zt4 = zero_vec<T4>();
   // Activation fragment kk of row 16j + c sits at xa[kk] + j * 16 * RB (the
   // swizzle of row 16j + c equals that of row c), so each tile's reads use
@@ -141,8 +141,8 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
   // One projection over tile J: NK activation fragments read from LDS
   // (already issued into xf), each feeding the products the caller asks for.
   // PEND: LDS reads issued after these NK that may stay outstanding.
-  auto project = [&](auto PEND, const T8 (&xf)[NK], bool with_q, bool with_kv, f32x4& aq,
-                     f32x4& ak, f32x4& av) {
+  auto project = [&](auto PEND, const T8 (&xf)[NK], bool with_q, bool with_kv, AccK32& aq,
+                     AccK32& ak, AccK32& av) {
     constexpr int pend = decltype(PEND)::value;
     static_for<NK>([&](auto KK) {
       constexpr int kk = decltype(KK)::value;
@@ -165,7 +165,7 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
   };
 
   // causal diagonal tile: key 4g + i visible to query c iff 4g + i <= c
-  f32x4 diag;
+  AccK32 diag;
 #pragma unroll
   for (int i = 0; i < 4; ++i) diag[i] = 4 * g + i <= c ? 0.f : -INFINITY;
 
@@ -209,7 +209,7 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
         constexpr int pend = j + 1 < NT ? NK : 0;
         if constexpr (j + 1 < NT) read_tile(std::integral_constant<int, j + 1>{}, st_off, xf[(j + 1) & 1]);
         const bool with_kv = j < kt_need;
-        f32x4 aq, ak = bk, av = bv;
+        AccK32 aq, ak = bk, av = bv;
         project(std::integral_constant<int, pend>{}, xf[j & 1], false, with_kv, aq, ak, av);
         // Keys at or past the key length are zeroed: their activation rows
         // are real query rows whose contents may be anything, and a hidden
@@ -272,7 +272,7 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
       {
         T8 xf[NK];
         read_tile(J, st_off, xf);
-        f32x4 aq = bq, ak, av;
+        AccK32 aq = bq, ak, av;
         project(std::integral_constant<int, 0>{}, xf, true, false, aq, ak, av);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -282,7 +282,7 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
       }
       constexpr int NKT = CAUSAL ? t + 1 : NT;  // key tiles computed at most
       const int klast = min(CAUSAL ? t : NT - 1, (L - 1) >> 4);
-      f32x4 o[HPW], lsum[HPW];
+      AccK32 o[HPW], lsum[HPW];
       float m[HPW];
 #pragma unroll
       for (int j = 0; j < HPW; ++j) {
@@ -293,14 +293,14 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
         const T8 qa = __builtin_shufflevector(qm, qm, 0, 1, 2, 3, 4, 5, 6, 7);
         const T4 lm = mine ? l4 : zt4;
         const T8 qb = __builtin_shufflevector(lm, lm, 0, 1, 2, 3, 4, 5, 6, 7);
-        f32x4 sc[NT];
+        AccK32 sc[NT];
         float mx = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
           if (kt > klast) break;
           // the causal diagonal starts from its constant mask; the tile
           // holding the key length then adds its offsets
-          const f32x4 init = (CAUSAL && kt == t) ? diag : zero4;
+          const AccK32 init = (CAUSAL && kt == t) ? diag : zero4;
           sc[kt] = mfma_k32(kf[kt], qa, init);
           sc[kt] = mfma_k32(kf[kt], qb, sc[kt]);
           if (kt == kL) {  // wave-uniform
@@ -315,7 +315,7 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
           mx = max3(mx, sc[kt][2], sc[kt][3]);
         }
         m[j] = group_max(mx) * c_log2;  // finite: key 0 is visible
-        auto probs = [&](const f32x4& sv, T4& hi, T4& lo) {
+        auto probs = [&](const AccK32& sv, T4& hi, T4& lo) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float pv = fast_exp2(fmaf(sv[i], c_log2, -m[j]));
@@ -355,7 +355,7 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
         }
       }
       // the O^T lane layout holds row `row`, columns 4g..4g+3: head gh's
-      const f32x4 os = HPW == 2 && gh == 1 ? o[HPW - 1] : o[0];
+      const AccK32 os = HPW == 2 && gh == 1 ? o[HPW - 1] : o[0];
       const float ls = HPW == 2 && gh == 1 ? lsum[HPW - 1][0] : lsum[0][0];  // every row holds the sum
       const float inv = __builtin_amdgcn_rcpf(ls);
       T4 ov;

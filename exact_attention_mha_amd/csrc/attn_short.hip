@@ -9,6 +9,8 @@
 // causal triangle (tile t needs t+1 key tiles) across the four waves.
 // Every query tile computes only the key tiles it can see: up to its own
 // diagonal when causal, never past the key length.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "launch.h"
 
@@ -80,11 +82,13 @@ attn_fwd_short(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __re
         qf[kc] = row < S ? *(const T8*)(Qh + row * D + 32 * kc + 8 * g) : zero_vec<T8>();
     }
 
-    f32x4 s[8];
+    // scores come from K = 16 products at d_h = 16, K = 32 ones otherwise
+    typedef std::conditional_t<D == 16, AccK16T<T>, AccK32> SAcc;
+    SAcc s[8];
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
-      s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s[kt] = SAcc::zero();
       if (kt < 2 * npair) {
         const int krow = 32 * (kt >> 1) + 8 * (c >> 2) + 4 * (kt & 1) + (c & 3);
         if constexpr (D == 16) {
@@ -110,9 +114,9 @@ attn_fwd_short(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __re
     const float m = mx * c_log2;  // -inf only when the tile sees no key (L == 0)
     const float msafe = npair > 0 ? m : 0.f;
     float ls = 0.f;
-    f32x4 o[NDT];
+    AccK32 o[NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < NDT; ++dt) o[dt] = AccK32::zero();
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       if (p < npair) {

@@ -125,7 +125,7 @@ attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __
   // computed except kL itself, which starts from `strad` (keys past L
   // hidden); the causal diagonal tile starts from `diag` (key <= row).
   const int kL = L >> 4;  // wave-uniform; L >= 1 below
-  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  typedef AccK16T<T> AccT;  // accumulator of this dtype's K = 16 product
 
   // one query tile, with its index a compile-time constant so that every
   // register array is indexed statically; the key tiles it sees are
@@ -143,12 +143,12 @@ attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __
     constexpr int NK = (QPW == NT && CAUSAL) ? j + 1 : NT;  // key tiles computed at most
     // last key tile with a visible key (wave-uniform)
     const int klast = min(CAUSAL ? t : NT - 1, (L - 1) >> 4);
-    f32x4 s[NT];
+    AccT s[NT];
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < NK; ++kt) {
       if (kt > klast) break;
-      f32x4 init = zero4;
+      AccT init = AccT::zero();
       if (kt == kL || (CAUSAL && kt == t)) {  // wave-uniform: a tile with hidden keys
         const int lim = min(L - 1, CAUSAL && kt == t ? row : S) - 16 * kt - 4 * g;
 #pragma unroll
@@ -159,7 +159,7 @@ attn_fwd_short16(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __
       mx = max3(mx, s[kt][2], s[kt][3]);
     }
     const float m = group_max(mx) * c_log2;  // finite: key 0 is visible
-    f32x4 o = {0.f, 0.f, 0.f, 0.f}, lsum = {0.f, 0.f, 0.f, 0.f};
+    AccT o = AccT::zero(), lsum = AccT::zero();
 #pragma unroll
     for (int kt = 0; kt < NK; ++kt) {
       if (kt > klast) break;

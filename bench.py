@@ -156,10 +156,12 @@ def cpu_baseline(w, q, k, v, kl, flops_per_pair_unit: int, budget_s: float = 12.
 
 
 def bench_backward(args, w, mha):
-    """One step = one mha_backward call (dq, dk, dv of sum(dout * out)) on
-    inputs resident in device memory, the forward's out / lse computed once
-    beforehand. FLOPs: 10 * d_h per visible pair (the five products S, dP,
-    dV, dQ, dK of 2 * d_h each)."""
+    """One step = one mha_backward_train call (dq, dk, dv of sum(dout * out),
+    the row term from the fp32 output of mha_forward_train) on inputs
+    resident in device memory, the forward's outputs computed once
+    beforehand. The same line carries mha_backward (row term from a pass over
+    the keys, from mha_forward's outputs) as a sub-record. FLOPs: 10 * d_h per
+    visible pair (the five products S, dP, dV, dQ, dK of 2 * d_h each)."""
     import torch
     import oracle
     from workloads import make_backward_inputs
@@ -173,36 +175,45 @@ def bench_backward(args, w, mha):
     kl_cpu = None if kl is None else kl.cpu()
     pairs = pair_count(w, kl_cpu)
     flops = 10 * w.D * pairs
+    _, lse_t, out32 = mha.forward_train(q, k, v, causal=w.causal, key_len=kl)
     out, lse = mha.forward(q, k, v, causal=w.causal, key_len=kl)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty_like(lse)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
+    def step_train():
+        mha.backward_train(q, k, v, out32, lse_t, dout, causal=w.causal, key_len=kl,
+                           dq=dq, dk=dk, dv=dv, delta=delta, stream=stream)
+
+    def step_exact():
         mha.backward(q, k, v, out, lse, dout, causal=w.causal, key_len=kl,
                      dq=dq, dk=dk, dv=dv, delta=delta, stream=stream)
 
-    t_w = time.perf_counter()
-    i = 0
-    while i < W or time.perf_counter() - t_w < WARMUP_S:
-        step()
-        i += 1
+    def timed(step):
+        t_w = time.perf_counter()
+        i = 0
+        while i < W or time.perf_counter() - t_w < WARMUP_S:
+            step()
+            i += 1
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(K):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ev_ms = e0.elapsed_time(e1)
-    ms_per_step = max(ev_ms, wall * 1e3) / K
-    k_avg_ms = ev_ms / K
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(K):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ev_ms = e0.elapsed_time(e1)
+        return max(ev_ms, wall * 1e3) / K, ev_ms / K
+
+    ms_exact, k_exact_ms = timed(step_exact)
+    ms_per_step, k_avg_ms = timed(step_train)
     tag = dtype_tag(w.dtype)
     achieved = flops / (k_avg_ms * 1e-3) / 1e12
     peak = PEAK_MFMA_TFLOPS[tag]
+    exact_achieved = flops / (k_exact_ms * 1e-3) / 1e12
     res = {
         "metric": "attention backward TFLOP/s (dq, dk, dv; 10*d_h flops per visible pair) "
                   "and % of MI355X MFMA roofline",
@@ -216,7 +227,9 @@ def bench_backward(args, w, mha):
                    "H_kv": w.H_kv or w.H, "S": w.S,
                    "d_h": w.D, "causal": w.causal,
                    "key_len": (None if w.key_len is None else list(w.key_len)), "seed": args.seed,
-                   "kernels": "row-term pass (bf16 only), dq, dk/dv", "parallelism": "single GPU"},
+                   "entry_point": "mha_backward_train (inputs from mha_forward_train: out32, lse)",
+                   "kernels": "row term dout . out32, then dq and dk/dv in one launch",
+                   "parallelism": "single GPU"},
         "roofline": {
             "bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 5),
@@ -227,6 +240,12 @@ def bench_backward(args, w, mha):
             "algorithmic_flops": flops, "kernel_source_hash": kernel_source_hash(BWD_SOURCES),
         },
         "flops_per_step": flops, "visible_pairs": pairs,
+        "subrecords": {"mha_backward": {
+            "entry_point": "mha_backward (inputs from mha_forward: out, lse)",
+            "kernels": "row-term pass over the keys, then dq and dk/dv in one launch",
+            "value": round(flops / (ms_exact * 1e-3) / 1e12, 4), "unit": "TFLOP/s",
+            "ms_per_step": round(ms_exact, 6), "kernel_avg_us": round(k_exact_ms * 1e3, 3),
+            "achieved": round(exact_achieved, 3), "frac": round(exact_achieved / peak, 5)}},
     }
     if not args.no_cpu_baseline:
         # the float64 oracle's backward on the whole workload

@@ -11,7 +11,10 @@ q, k, v: contiguous [B, H, S, d_h] tensors on the GPU (float32, float16 or
 bfloat16), d_h in {8, 16, 32, 64, 128, 256} (8: fp16 / bf16 only); key_len: None or an int32 GPU
 tensor [B] of right-padded key lengths. backward() gives dq, dk, dv;
 qkv_attention() takes the activations and the QKV projection weights
-instead of q, k, v, for short sequences of 16-wide heads.
+instead of q, k, v, for short sequences of 16-wide heads. For training,
+forward_train() also returns the output in fp32, from which backward_train()
+takes the softmax row term with one pass over dout instead of a pass over the
+keys.
 """
 
 from __future__ import annotations
@@ -21,7 +24,8 @@ import os
 from typing import Optional, Tuple
 
 __all__ = [
-    "forward", "backward", "backward_noalloc", "qkv_attention", "load", "library_path",
+    "forward", "forward_train", "backward", "backward_train", "backward_noalloc",
+    "qkv_attention", "load", "library_path",
     "library_built", "MAX_NOALLOC_ROWS",
     "select_variant", "VARIANTS", "DTYPES", "MhaError",
 ]
@@ -79,6 +83,10 @@ def load() -> ctypes.CDLL:
     lib.mha_backward_grouped.restype = ctypes.c_int
     lib.mha_backward_noalloc.argtypes = [vp] * 9 + [i64] * 4 + [ctypes.c_int, vp, ctypes.c_int, vp]
     lib.mha_backward_noalloc.restype = ctypes.c_int
+    lib.mha_forward_train.argtypes = [vp] * 6 + [i64] * 5 + [ctypes.c_int, vp, ctypes.c_int, vp]
+    lib.mha_forward_train.restype = ctypes.c_int
+    lib.mha_backward_train.argtypes = [vp] * 10 + [i64] * 5 + [ctypes.c_int, vp, ctypes.c_int, vp]
+    lib.mha_backward_train.restype = ctypes.c_int
     lib.mha_qkv_attention.argtypes = [vp] * 5 + [i64] * 4 + [ctypes.c_int, vp, ctypes.c_int, vp]
     lib.mha_qkv_attention.restype = ctypes.c_int
     lib.mha_select_variant.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
@@ -191,6 +199,58 @@ def forward(q, k, v, causal: bool = False, key_len=None, out=None, lse=None,
     return out, lse
 
 
+def forward_train(q, k, v, causal: bool = False, key_len=None, out=None, lse=None,
+                  out32=None, stream=None):
+    """forward() that also writes the output in fp32 (mha_forward_train).
+
+    Args as forward() (contiguous q and k, v with H or H_kv heads, H_kv
+    dividing H; float16 or bfloat16); out32: optional preallocated contiguous
+    float32 [B, H, S, d_h].
+    Returns:
+      (out, lse, out32) -- pass lse and out32 to backward_train().
+    """
+    import torch
+
+    lib = load()
+    B, H, S, D = q.shape
+    H_kv = k.shape[1] if k.dim() == 4 else -1
+    if H_kv < 1 or H % H_kv or k.shape != (B, H_kv, S, D) or v.shape != k.shape:
+        raise ValueError(f"k, v must be [B, H_kv, S, d_h] with H_kv dividing H={H}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor of the dtype of q")
+    dcode = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if out32 is None:
+        out32 = torch.empty((B, H, S, D), dtype=torch.float32, device=q.device)
+    for name, t, shp, dt in (("out", out, q.shape, q.dtype), ("lse", lse, (B, H, S), torch.float32),
+                             ("out32", out32, q.shape, torch.float32)):
+        if t.shape != shp or t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} GPU tensor of shape {tuple(shp)}")
+    kl_ptr = _key_len_ptr(key_len, B)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    status = lib.mha_forward_train(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), out32.data_ptr(),
+        B, H, H_kv, S, D, int(bool(causal)), kl_ptr, dcode, st.cuda_stream)
+    if status != 0:
+        raise MhaError("mha_forward_train", status, lib.mha_status_string(status).decode())
+    return out, lse, out32
+
+
+def _key_len_ptr(key_len, B):
+    import torch
+
+    if key_len is None:
+        return None
+    if (key_len.dtype != torch.int32 or key_len.shape != (B,) or not key_len.is_cuda
+            or not key_len.is_contiguous()):
+        raise ValueError("key_len must be a contiguous int32 GPU tensor [B]")
+    return key_len.data_ptr()
+
+
 def backward(q, k, v, out, lse, dout, causal: bool = False, key_len=None,
              dq=None, dk=None, dv=None, delta=None, stream=None):
     """Gradients (dq, dk, dv) of sum(dout * out) through the attention forward.
@@ -208,6 +268,19 @@ def backward(q, k, v, out, lse, dout, causal: bool = False, key_len=None,
     Returns:
       (dq, dk, dv).
     """
+    return _backward(q, k, v, out, None, lse, dout, causal, key_len, dq, dk, dv, delta, stream)
+
+
+def backward_train(q, k, v, out32, lse, dout, causal: bool = False, key_len=None,
+                   dq=None, dk=None, dv=None, delta=None, stream=None):
+    """backward() with the row term D = rowsum(dout * out32) taken from
+    forward_train()'s fp32 output (mha_backward_train): one pass over dout
+    and out32 replaces the pass over the keys. Other arguments as backward().
+    Returns (dq, dk, dv)."""
+    return _backward(q, k, v, None, out32, lse, dout, causal, key_len, dq, dk, dv, delta, stream)
+
+
+def _backward(q, k, v, out, out32, lse, dout, causal, key_len, dq, dk, dv, delta, stream):
     import torch
 
     lib = load()
@@ -215,8 +288,13 @@ def backward(q, k, v, out, lse, dout, causal: bool = False, key_len=None,
     H_kv = k.shape[1] if k.dim() == 4 else -1
     if H_kv < 1 or H % H_kv or k.shape != (B, H_kv, S, D) or v.shape != k.shape:
         raise ValueError(f"k, v must be [B, H_kv, S, d_h] with H_kv dividing H={H}")
-    for name, t, shp in (("q", q, q.shape), ("k", k, k.shape), ("v", v, k.shape),
-                         ("out", out, q.shape), ("dout", dout, q.shape)):
+    checks = [("q", q, q.shape), ("k", k, k.shape), ("v", v, k.shape), ("dout", dout, q.shape)]
+    if out32 is None:
+        checks.append(("out", out, q.shape))
+    elif (out32.shape != q.shape or out32.dtype != torch.float32 or not out32.is_cuda
+          or not out32.is_contiguous()):
+        raise ValueError("out32 must be forward_train()'s contiguous float32 GPU tensor")
+    for name, t, shp in checks:
         if t.shape != shp or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous GPU tensor of shape {tuple(shp)} "
                              f"and the dtype of q")
@@ -237,19 +315,16 @@ def backward(q, k, v, out, lse, dout, causal: bool = False, key_len=None,
     elif (delta.shape != (B, H, S) or delta.dtype != torch.float32 or not delta.is_cuda
           or not delta.is_contiguous()):
         raise ValueError("delta must be a contiguous float32 GPU tensor [B, H, S]")
-    kl_ptr = None
-    if key_len is not None:
-        if (key_len.dtype != torch.int32 or key_len.shape != (B,) or not key_len.is_cuda
-                or not key_len.is_contiguous()):
-            raise ValueError("key_len must be a contiguous int32 GPU tensor [B]")
-        kl_ptr = key_len.data_ptr()
+    kl_ptr = _key_len_ptr(key_len, B)
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
-    status = lib.mha_backward_grouped(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+    fn = "mha_backward_grouped" if out32 is None else "mha_backward_train"
+    status = getattr(lib, fn)(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(),
+        out.data_ptr() if out32 is None else out32.data_ptr(), dout.data_ptr(),
         lse.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
         delta.data_ptr(), B, H, H_kv, S, D, int(bool(causal)), kl_ptr, dcode, st.cuda_stream)
     if status != 0:
-        raise MhaError("mha_backward_grouped", status, lib.mha_status_string(status).decode())
+        raise MhaError(fn, status, lib.mha_status_string(status).decode())
     return tuple(grads)
 
 

@@ -36,12 +36,13 @@
 //
 // A 32-row pair of an LDS operand block is read both as 16-row tiles (one
 // 128-bit row read per lane) and transposed (ds_read_b64_tr_b16 over 4 rows
-// per lane group). Row c of tile h of the pair is stored at LDS row
-// 16h + 2(c % 8) + c / 8 of the pair: a tile read then covers 16 distinct
-// padded rows, and each half-wave of a transposed read 8 rows of one parity,
-// which keeps both kinds of read free of bank conflicts. In the contraction
-// over a pair, k-slot 8g + 4h + i of lane group g stands for row 16h + 4g + i
-// of the pair, in both operands.
+// per lane group). From d_h = 32 on, rows keep their order and each padded
+// row holds d_h + 16 elements: the LDS bank-conflict counters read zero for
+// both kinds of read in that layout (with d_h + 8, the row reads take two
+// passes). At d_h = 16 row c of tile h of the pair is stored at LDS row
+// 16h + 2(c % 8) + c / 8 of the pair, with d_h + 8 per row. In the
+// contraction over a pair, k-slot 8g + 4h + i of lane group g stands for row
+// 16h + 4g + i of the pair, in both operands.
 #include <type_traits>
 
 #include "attn_common.h"
@@ -49,8 +50,8 @@
 
 namespace mha {
 
-// LDS row (within a 32-row pair) of pair row x, and the pair row stored at
-// LDS row r.
+// d_h = 16: LDS row (within a 32-row pair) of pair row x, and the pair row
+// stored at LDS row r.
 __device__ __forceinline__ int bwd_lds_row(int x) {
   const int c = x & 15;
   return (x & 16) + 2 * (c & 7) + (c >> 3);
@@ -61,12 +62,12 @@ __device__ __forceinline__ int bwd_row_at(int r) {
 }
 
 // Per-lane DMA slots of an operand block of NR rows x D columns in the
-// padded pair-permuted LDS layout: fills the source byte offsets (relative
-// to the block's first row; kOutOfRange for pad slots) of this wave's slots.
+// padded LDS layout above: fills the source byte offsets (relative to the
+// block's first row; kOutOfRange for pad slots) of this wave's slots.
 template <typename T, int D, int NR, int NW>
 struct BwdTile {
-  static constexpr int STR = D + 8;
-  static constexpr int SPR = D / 8 + 1;
+  static constexpr int STR = D >= 32 ? D + 16 : D + 8;
+  static constexpr int SPR = STR / 8;
   static constexpr int SLOTS = NR * SPR;
   static constexpr int NI = (SLOTS + 63) / 64;
   static constexpr int ELEMS = NI * 64 * 8;  // whole DMA instructions
@@ -78,7 +79,7 @@ struct BwdTile {
       const int slot = (wave + i * NW) * 64 + lane;
       const int row = slot / SPR, j = slot - row * SPR;
       const bool live = slot < SLOTS && j < D / 8;
-      off[i] = live ? (32 * (row >> 5) + bwd_row_at(row & 31)) * RB + 16 * j : kOutOfRange;
+      off[i] = live ? (D >= 32 ? row : 32 * (row >> 5) + bwd_row_at(row & 31)) * RB + 16 * j : kOutOfRange;
     }
   }
   __device__ static void copy(rsrc_t r, T* dst, const int (&off)[NIW], int wave, int soff) {
@@ -206,8 +207,8 @@ __device__ __forceinline__ void bwd_dq_body(
 
     // per-lane LDS offsets (elements): tile row c of a pair (row reads), and
     // the transposed read of lane group g (rows 4g + c/4, column 4(c%4))
-    const int rrow = bwd_lds_row(c) * STR;
-    const int trow = bwd_lds_row(4 * g + (c >> 2)) * STR + 4 * (c & 3);
+    const int rrow = (D >= 32 ? c : bwd_lds_row(c)) * STR;
+    const int trow = (D >= 32 ? 4 * g + (c >> 2) : bwd_lds_row(4 * g + (c >> 2))) * STR + 4 * (c & 3);
 
     for (int kb = 0; kb < nblk; ++kb) {
       const int k0 = kb * BK;
@@ -473,8 +474,8 @@ __device__ __forceinline__ void bwd_dkv_body(
     };
     dma_block(0, 0);
 
-    const int rrow = bwd_lds_row(c) * STR;
-    const int trow = bwd_lds_row(4 * g + (c >> 2)) * STR + 4 * (c & 3);
+    const int rrow = (D >= 32 ? c : bwd_lds_row(c)) * STR;
+    const int trow = (D >= 32 ? 4 * g + (c >> 2) : bwd_lds_row(4 * g + (c >> 2))) * STR + 4 * (c & 3);
 
     const int n_it = group * nblk;
     for (int it = 0; it < n_it; ++it) {
@@ -665,6 +666,47 @@ attn_bwd_both(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   }
 }
 
+// Row term from the forward's fp32 output: D = rowsum(dO * O32) for every
+// query row, in fp32. Each lane takes 8 consecutive columns of one row (a
+// 16-byte dO load, two 16-byte O32 loads), D / 8 lanes per row, reduced
+// across those lanes. Rows are contiguous over (batch, head, position).
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+attn_bwd_rowdot(const T* __restrict__ dOp, const float* __restrict__ O32p, float* __restrict__ Dp,
+                int64_t rows) {
+  typedef typename Vec<T>::x8 T8;
+  constexpr int LPR = D / 8;         // lanes per row
+  constexpr int RPB = 256 / LPR;     // rows per workgroup
+  static_assert(D % 8 == 0 && LPR <= 64, "row width");
+  const int tid = threadIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;
+  const int col = 8 * (tid % LPR);
+  float acc = 0.f;
+  if (row < rows) {
+    const T8 d = *(const T8*)(dOp + row * D + col);
+    const f32x4 o0 = *(const f32x4*)(O32p + row * D + col);
+    const f32x4 o1 = *(const f32x4*)(O32p + row * D + col + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = fmaf(to_f(d[i]), o0[i], acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = fmaf(to_f(d[4 + i]), o1[i], acc);
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (row < rows && tid % LPR == 0) Dp[row] = acc;
+}
+
+template <typename T, int D>
+static hipError_t launch_rowdot(const BwdParams& p, hipStream_t s) {
+  constexpr int RPB = 256 / (D / 8);
+  const int64_t rows = (int64_t)p.B * p.H * p.S;
+  const int64_t nwg = (rows + RPB - 1) / RPB;
+  if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((attn_bwd_rowdot<T, D>), dim3((unsigned)nwg), dim3(256), 0, s, (const T*)p.dout,
+                     p.out32, p.delta, rows);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- launchers
 template <typename T, int D, int NQT, int NW, int BK, int NKTW, int BQb>
 static hipError_t launch_bwd_one(const BwdParams& p, hipStream_t s) {
@@ -675,11 +717,17 @@ static hipError_t launch_bwd_one(const BwdParams& p, hipStream_t s) {
   const int64_t wq = (int64_t)p.B * p.H * n_qblk, wk = (int64_t)p.B * (p.H / p.group) * n_kblk;
   if (wq > 0x7fffffffLL || wk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const float scale = 1.f / sqrtf((float)p.D);
-  // the row pass writes D, then dQ and dK / dV run in one launch behind it
-  hipLaunchKernelGGL((attn_bwd_dq<T, D, NQT, NW, BK, kRowPass>), dim3((unsigned)wq), dim3(NW * 64), 0, s,
-                     (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.dout, p.lse,
-                     (T*)p.dq, p.delta, p.key_len, p.H, p.S, p.causal, n_qblk, p.c_log2, scale, p.group);
-  hipError_t e = hipGetLastError();
+  // the row pass (or, given the fp32 output, its dot product with dO)
+  // writes D, then dQ and dK / dV run in one launch behind it
+  hipError_t e;
+  if (p.out32) {
+    e = launch_rowdot<T, D>(p, s);
+  } else {
+    hipLaunchKernelGGL((attn_bwd_dq<T, D, NQT, NW, BK, kRowPass>), dim3((unsigned)wq), dim3(NW * 64), 0, s,
+                       (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.dout, p.lse,
+                       (T*)p.dq, p.delta, p.key_len, p.H, p.S, p.causal, n_qblk, p.c_log2, scale, p.group);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   const int64_t wk_pad = (wk + 7) / 8 * 8;
   if (wk_pad + wq > 0x7fffffffLL) return hipErrorInvalidConfiguration;

@@ -198,6 +198,9 @@ template <typename V>
 __device__ __forceinline__ void buf_store8(V v, rsrc_t r, int voff) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff, 0, 0);
 }
+__device__ __forceinline__ void buf_store16(f32x4 v, rsrc_t r, int voff) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, 0, 0);
+}
 __device__ __forceinline__ void buf_store4(float v, rsrc_t r, int voff) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, voff, 0, 0);
 }

@@ -69,8 +69,9 @@ __device__ __forceinline__ int v_key_of_row(int rho) {
 template <typename T, int D, int NQT, int NW, int BK, bool SUM_MFMA, int NST, bool STALE = false>
 __global__ void __launch_bounds__(NW * 64, NW == 4 ? 2 : 1)
 attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
-              T* __restrict__ Op, float* __restrict__ LSEp, const int32_t* __restrict__ key_len,
-              int H, int S, int causal, int n_qblk, float c_log2, Layout lay) {
+              T* __restrict__ Op, float* __restrict__ LSEp, float* __restrict__ O32p,
+              const int32_t* __restrict__ key_len, int H, int S, int causal, int n_qblk,
+              float c_log2, Layout lay) {
   typedef typename Vec<T>::x8 T8;
   typedef typename Vec<T>::x4 T4;
   constexpr int STR = D + 8;             // padded LDS row stride (elements)
@@ -125,6 +126,8 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
 
   const rsrc_t ro = make_rsrc(Oh, span(S, RO));
   const rsrc_t rl = make_rsrc(LSEp + (int64_t)bh * S, (uint32_t)S * 4);
+  // fp32 copy of the output (training forward): contiguous [B, H, S, D]
+  const rsrc_t r32 = make_rsrc(O32p + (int64_t)bh * S * D, (uint32_t)S * D * 4);
 
   if (nblk == 0) {  // no visible key (L == 0): out = 0, lse = -inf
     if (wave_live) {
@@ -134,6 +137,10 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
           buf_store8(zero_vec<T4>(), ro, kHalf && g >= 2 ? kOutOfRange : row * RO + (16 * dt + 4 * g) * 2);
+        if (O32p)
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            buf_store16(f32x4{0.f, 0.f, 0.f, 0.f}, r32, kHalf && g >= 2 ? kOutOfRange : (row * D + 16 * dt + 4 * g) * 4);
         if (LSEp) buf_store4(-INFINITY, rl, g == 0 ? row * 4 : kOutOfRange);
       }
     }
@@ -457,6 +464,7 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
 #pragma unroll
         for (int i = 0; i < 4; ++i) ov[i] = to_t<T>(o[t][dt][i] * inv);
         buf_store8(ov, ro, kHalf && g >= 2 ? kOutOfRange : row * RO + (16 * dt + 4 * g) * 2);
+        if (O32p) buf_store16(o[t][dt].vec() * inv, r32, kHalf && g >= 2 ? kOutOfRange : (row * D + 16 * dt + 4 * g) * 4);
       }
       if (LSEp) buf_store4((m_run[t] + fast_log2(l)) * kLn2, rl, g == 0 ? row * 4 : kOutOfRange);
     }
@@ -498,8 +506,9 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
 template <typename T, int D, int NQT, int NW, int BK, int MINB>
 __global__ void __launch_bounds__(NW * 64, MINB)
 attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
-              T* __restrict__ Op, float* __restrict__ LSEp, const int32_t* __restrict__ key_len,
-              int H, int S, int causal, int n_qblk, float c_log2, Layout lay) {
+              T* __restrict__ Op, float* __restrict__ LSEp, float* __restrict__ O32p,
+              const int32_t* __restrict__ key_len, int H, int S, int causal, int n_qblk,
+              float c_log2, Layout lay) {
   typedef typename Vec<T>::x8 T8;
   typedef typename Vec<T>::x4 T4;
   constexpr int NST = 4;
@@ -551,6 +560,8 @@ attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
 
   const rsrc_t ro = make_rsrc(Oh, span(S, RO));
   const rsrc_t rl = make_rsrc(LSEp + (int64_t)bh * S, (uint32_t)S * 4);
+  // fp32 copy of the output (training forward): contiguous [B, H, S, D]
+  const rsrc_t r32 = make_rsrc(O32p + (int64_t)bh * S * D, (uint32_t)S * D * 4);
 
   if (nblk == 0) {  // no visible key (L == 0): out = 0, lse = -inf
     if (wave_live) {
@@ -559,6 +570,9 @@ attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
         const int row = wq0 + 16 * t + c;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) buf_store8(zero_vec<T4>(), ro, row * RO + (16 * dt + 4 * g) * 2);
+        if (O32p)
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) buf_store16(f32x4{0.f, 0.f, 0.f, 0.f}, r32, (row * D + 16 * dt + 4 * g) * 4);
         if (LSEp) buf_store4(-INFINITY, rl, g == 0 ? row * 4 : kOutOfRange);
       }
     }
@@ -871,6 +885,7 @@ attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
 #pragma unroll
         for (int i = 0; i < 4; ++i) ov[i] = to_t<T>(o[t][dt][i] * inv);
         buf_store8(ov, ro, row * RO + (16 * dt + 4 * g) * 2);
+        if (O32p) buf_store16(o[t][dt].vec() * inv, r32, (row * D + 16 * dt + 4 * g) * 4);
       }
       if (LSEp) buf_store4((m_run[t] + fast_log2(l)) * kLn2, rl, g == 0 ? row * 4 : kOutOfRange);
     }
@@ -884,8 +899,8 @@ static hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   const int64_t n_wg = (int64_t)p.B * p.H * n_qblk;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((attn_fwd_mfma<T, D, NQT, NW, BK, SM, NST, STALE>), dim3((unsigned)n_wg), dim3(NW * 64), 0, s,
-                     (const T*)p.q, (const T*)p.k, (const T*)p.v, (T*)p.out, p.lse, p.key_len,
-                     p.H, p.S, p.causal, n_qblk, p.c_log2, p.lay);
+                     (const T*)p.q, (const T*)p.k, (const T*)p.v, (T*)p.out, p.lse, p.out32,
+                     p.key_len, p.H, p.S, p.causal, n_qblk, p.c_log2, p.lay);
   return hipGetLastError();
 }
 
@@ -896,8 +911,8 @@ static hipError_t launch_pipe(const AttnParams& p, hipStream_t s) {
   const int64_t n_wg = (int64_t)p.B * p.H * n_qblk;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((attn_fwd_pipe<T, D, NQT, NW, BK, MINB>), dim3((unsigned)n_wg), dim3(NW * 64), 0, s,
-                     (const T*)p.q, (const T*)p.k, (const T*)p.v, (T*)p.out, p.lse, p.key_len,
-                     p.H, p.S, p.causal, n_qblk, p.c_log2, p.lay);
+                     (const T*)p.q, (const T*)p.k, (const T*)p.v, (T*)p.out, p.lse, p.out32,
+                     p.key_len, p.H, p.S, p.causal, n_qblk, p.c_log2, p.lay);
   return hipGetLastError();
 }
 

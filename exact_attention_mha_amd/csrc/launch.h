@@ -38,6 +38,8 @@ struct AttnParams {
   int dtype;               // enum mha_dtype
   float c_log2;            // log2(e) / sqrt(d_h)
   Layout lay;              // strides (contiguous unless from mha_forward_strided)
+  float* out32 = nullptr;  // nullable: the output in fp32, contiguous [B, H, S, D]
+                           // (matrix-core kernels only)
 };
 
 // Backward: dq, dk, dv of sum(dout * out); delta is the caller's float
@@ -60,6 +62,8 @@ struct BwdParams {
   int dtype;
   float c_log2;
   int group;               // query heads per key / value head (k, v, dk, dv have H / group)
+  const float* out32 = nullptr;  // nullable: the forward's output in fp32 ([B, H, S, D]);
+                                 // when given, D = rowsum(dout * out32) replaces the row pass
 };
 
 // Attention fed by its own QKV projection (d_h = hd in {8, 16}, S <= 128):

@@ -166,18 +166,62 @@ int mha_forward(const void* q, const void* k, const void* v, void* out, float* l
                              MHA_VARIANT_AUTO);
 }
 
-int mha_backward_grouped(const void* q, const void* k, const void* v, const void* out,
-                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                         float* delta, int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t d_h,
-                         int causal, const int32_t* key_len, int dtype, void* stream) {
+int mha_forward_train(const void* q, const void* k, const void* v, void* out, float* lse,
+                      float* out32, int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t d_h,
+                      int causal, const int32_t* key_len, int dtype, void* stream) {
+  const int st = validate(q, k, v, out, lse, B, H, S, d_h, key_len, dtype);
+  if (st != MHA_OK) return st;
+  if (dtype == MHA_F32) return MHA_ERR_UNSUPPORTED;
+  if (H_kv <= 0 || (H > 0 && H % H_kv != 0)) return MHA_ERR_SHAPE;
+  if (B == 0 || H == 0 || S == 0) return MHA_OK;
+  if (!lse || !out32) return MHA_ERR_NULL;
+  if (!aligned(out32, 16)) return MHA_ERR_MISALIGNED;
+  if (S * d_h * 4 >= (int64_t)1 << 31) return MHA_ERR_SHAPE;  // per-head fp32 byte offsets
+
+  mha::AttnParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.out32 = out32;
+  p.key_len = key_len;
+  p.B = (int)B;
+  p.H = (int)H;
+  p.S = (int)S;
+  p.D = (int)d_h;
+  p.causal = causal ? 1 : 0;
+  p.dtype = dtype;
+  p.c_log2 = (float)(1.4426950408889634074 / sqrt((double)d_h));
+  p.lay = mha::contiguous_layout((int)H, (int)S, (int)d_h);
+  p.lay.k_b = p.lay.v_b = H_kv * S * d_h;  // k, v: contiguous [B, H_kv, S, d_h]
+  p.lay.group = (int)(H / H_kv);
+  // the matrix-core kernels (the only ones that write out32), by head count
+  const bool small = B * H * ((S + 127) / 128) < 512;
+  const hipError_t e = small ? mha::launch_mfma_small(p, (hipStream_t)stream)
+                             : mha::launch_mfma(p, (hipStream_t)stream);
+  if (e == hipErrorInvalidConfiguration) return MHA_ERR_SHAPE;
+  return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
+}
+
+}  // extern "C"
+
+namespace {
+
+// mha_backward_grouped and mha_backward_train: `out` (not read) or `out32`
+// (the row term's source) identifies the forward output.
+int backward_impl(const void* q, const void* k, const void* v, const void* out,
+                  const float* out32, const void* dout, const float* lse, void* dq, void* dk,
+                  void* dv, float* delta, int64_t B, int64_t H, int64_t H_kv, int64_t S,
+                  int64_t d_h, int causal, const int32_t* key_len, int dtype, void* stream) {
   int st = validate(q, k, v, dq, lse, B, H, S, d_h, key_len, dtype);
   if (st != MHA_OK) return st;
   if (dtype == MHA_F32 || d_h == 8) return MHA_ERR_UNSUPPORTED;
   if (H_kv <= 0 || (H > 0 && H % H_kv != 0)) return MHA_ERR_SHAPE;
   if (B == 0 || H == 0 || S == 0) return MHA_OK;
-  if (!out || !dout || !lse || !dk || !dv || !delta) return MHA_ERR_NULL;
-  if (!aligned(out, 16) || !aligned(dout, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
-      !aligned(delta, 4))
+  if (!(out || out32) || !dout || !lse || !dk || !dv || !delta) return MHA_ERR_NULL;
+  if ((out && !aligned(out, 16)) || (out32 && !aligned(out32, 16)) || !aligned(dout, 16) ||
+      !aligned(dk, 16) || !aligned(dv, 16) || !aligned(delta, 4))
     return MHA_ERR_MISALIGNED;
 
   mha::BwdParams p;
@@ -200,9 +244,30 @@ int mha_backward_grouped(const void* q, const void* k, const void* v, const void
   p.dtype = dtype;
   p.c_log2 = (float)(1.4426950408889634074 / sqrt((double)d_h));
   p.group = (int)(H / H_kv);
+  p.out32 = out32;
   const hipError_t e = mha::launch_bwd(p, (hipStream_t)stream);
   if (e == hipErrorInvalidConfiguration) return MHA_ERR_SHAPE;
   return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mha_backward_grouped(const void* q, const void* k, const void* v, const void* out,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         float* delta, int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t d_h,
+                         int causal, const int32_t* key_len, int dtype, void* stream) {
+  return backward_impl(q, k, v, out, nullptr, dout, lse, dq, dk, dv, delta, B, H, H_kv, S, d_h,
+                       causal, key_len, dtype, stream);
+}
+
+int mha_backward_train(const void* q, const void* k, const void* v, const float* out32,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                       float* delta, int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t d_h,
+                       int causal, const int32_t* key_len, int dtype, void* stream) {
+  return backward_impl(q, k, v, nullptr, out32, dout, lse, dq, dk, dv, delta, B, H, H_kv, S, d_h,
+                       causal, key_len, dtype, stream);
 }
 
 int mha_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
@@ -334,6 +399,6 @@ const char* mha_status_string(int status) {
   return "unknown status";
 }
 
-int mha_version(void) { return 106; }
+int mha_version(void) { return 107; }
 
 }  // extern "C"

@@ -114,6 +114,38 @@ int mha_forward_variant(const void* q, const void* k, const void* v, void* out, 
                         const int32_t* key_len, int dtype, void* stream, int variant);
 
 /*
+ * mha_forward_train -- mha_forward that also keeps the output in fp32, for
+ * the backward's row term (mha_backward_train).
+ *
+ * The fused backward of rustingstudio "brain/docs/baseline" ("Fused
+ * attention") takes its softmax row term from dout and the forward output,
+ * D = rowsum(dout * O). With O rounded to fp16 or bf16 that term is off by a
+ * rounding of O, which dq and dk amplify where the softmax is peaked; the
+ * output before that rounding (O / l in fp32) keeps it within the accuracy
+ * rule over the range of scores stated for mha_backward, and lets the
+ * backward form D with one pass over dout and out32 instead of a pass over
+ * the keys.
+ *
+ *   out32    device pointer, contiguous fp32 [B, H, S, d_h], 16-byte aligned;
+ *            written in full (rows with no visible key get 0). Required.
+ *   lse      required (the backward needs it).
+ *   H_kv     key / value heads (>= 1, dividing H): k and v are contiguous
+ *            [B, H_kv, S, d_h] and query head h uses head h / (H / H_kv), as
+ *            in mha_forward_strided (H_kv = H: ordinary multi-head).
+ *   other arguments as for mha_forward; dtype must be MHA_F16 or MHA_BF16.
+ *
+ * Runs the matrix-core kernels (out is identical to what mha_forward_variant
+ * writes with MHA_VARIANT_MFMA or MHA_VARIANT_MFMA_SMALL, chosen by head
+ * count as mha_forward does for long sequences). Returns MHA_ERR_UNSUPPORTED
+ * for fp32 inputs, MHA_ERR_NULL without lse or out32, MHA_ERR_SHAPE when one
+ * head of out32 spans 2^31 bytes or more or H_kv does not divide H. Ownership, asynchrony and error
+ * behaviour as for mha_forward.
+ */
+int mha_forward_train(const void* q, const void* k, const void* v, void* out, float* lse,
+                      float* out32, int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t d_h,
+                      int causal, const int32_t* key_len, int dtype, void* stream);
+
+/*
  * mha_forward_strided -- mha_forward over strided views, with grouped
  * key / value heads.
  *
@@ -226,6 +258,32 @@ int mha_backward_grouped(const void* q, const void* k, const void* v, const void
                          int causal, const int32_t* key_len, int dtype, void* stream);
 
 /*
+ * mha_backward_train -- mha_backward_grouped with the row term taken from
+ * the fp32 output of mha_forward_train: D = rowsum(dout * out32) in fp32,
+ * one pass over dout and out32 (rustingstudio "brain/docs/baseline",
+ * "Fused attention": the row sum comes from dO and O), then the same dq and
+ * dk / dv launch as mha_backward_grouped.
+ *
+ *   out32    the out32 of mha_forward_train for exactly these inputs and
+ *            mask: device pointer, contiguous fp32 [B, H, S, d_h], 16-byte
+ *            aligned. Read only.
+ *   delta    caller-owned float workspace [B, H, S], 4-byte aligned;
+ *            overwritten with D.
+ *   other arguments as mha_backward_grouped (H_kv = H for ordinary
+ *   multi-head attention).
+ *
+ * Precision as mha_backward for bf16 (the forward's probabilities enter its
+ * value product as a head and a remainder, so out32 is the exact output to
+ * fp32 rounding); for fp16 out32 carries the single rounding of the
+ * probabilities in that product, which stays within the accuracy rule over
+ * the range of scores stated for mha_backward. MHA_ERR_NULL without out32.
+ */
+int mha_backward_train(const void* q, const void* k, const void* v, const float* out32,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                       float* delta, int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t d_h,
+                       int causal, const int32_t* key_len, int dtype, void* stream);
+
+/*
  * mha_qkv_attention -- attention fed by its own QKV projection, for short
  * sequences of 16- or 8-wide heads (devpost "gpu-transformer-optimization",
  * section 2.2: the fused QKV projection, and the fused QKV-attention program
@@ -274,7 +332,8 @@ const char* mha_status_string(int status);
 
 /* Library ABI version (major * 100 + minor); 101 adds mha_backward, 102
  * mha_forward_strided, 103 mha_backward_grouped, 104 mha_qkv_attention,
- * 105 d_h = 8 (mha_forward*, mha_qkv_attention). */
+ * 105 d_h = 8 (mha_forward*, mha_qkv_attention), 106 mha_backward_noalloc,
+ * 107 mha_forward_train and mha_backward_train. */
 int mha_version(void);
 
 #ifdef __cplusplus

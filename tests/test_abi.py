@@ -189,6 +189,49 @@ def test_grouped_backward_validation(mha):
     assert lib.mha_backward_grouped(*args, 0, 4, 2, 16, 64, 0, None, 1, None) == 0  # empty
 
 
+def _fwd_train(lib, q=0x1000, k=0x2000, v=0x3000, out=0x4000, lse=0x5000, out32=0x6000, B=1,
+               H=2, H_kv=1, S=16, D=64, causal=0, key_len=None, dtype=1):
+    return lib.mha_forward_train(q, k, v, out, lse, out32, B, H, H_kv, S, D, causal, key_len,
+                                 dtype, None)
+
+
+def test_forward_train_validation_codes(mha):
+    """The training forward checks its arguments like mha_forward, and also
+    needs lse and the fp32 output buffer (16-byte aligned); no kernel runs."""
+    lib = mha.load()
+    assert lib.mha_version() >= 107
+    assert _fwd_train(lib, lse=None) == 1
+    assert _fwd_train(lib, out32=None) == 1
+    assert _fwd_train(lib, q=None) == 1
+    assert _fwd_train(lib, out32=0x6004) == 4
+    assert _fwd_train(lib, dtype=0) == 3          # fp32 inputs: no training path
+    assert _fwd_train(lib, D=48) == 3
+    assert _fwd_train(lib, S=-1) == 2
+    assert _fwd_train(lib, S=1 << 23, D=64) == 2  # one head of out32 spans 2^31 bytes
+    assert _fwd_train(lib, H_kv=3) == 2           # H_kv must divide H
+    assert _fwd_train(lib, H_kv=0) == 2
+    assert _fwd_train(lib, B=0, lse=None) == 0    # empty: no-op
+
+
+def _bwd_train(lib, q=0x1000, k=0x2000, v=0x3000, out32=0x4000, dout=0x5000, lse=0x6000,
+               dq=0x7000, dk=0x8000, dv=0x9000, delta=0xa000, B=1, H=2, H_kv=1, S=16, D=64,
+               causal=0, key_len=None, dtype=1):
+    return lib.mha_backward_train(q, k, v, out32, dout, lse, dq, dk, dv, delta, B, H, H_kv, S, D,
+                                  causal, key_len, dtype, None)
+
+
+def test_backward_train_validation_codes(mha):
+    lib = mha.load()
+    assert _bwd_train(lib, out32=None) == 1
+    assert _bwd_train(lib, dout=None) == 1
+    assert _bwd_train(lib, delta=None) == 1
+    assert _bwd_train(lib, out32=0x4008) == 4
+    assert _bwd_train(lib, H_kv=3) == 2
+    assert _bwd_train(lib, D=8) == 3
+    assert _bwd_train(lib, dtype=0) == 3
+    assert _bwd_train(lib, B=0, out32=None) == 0  # empty: no-op
+
+
 def _qkv(lib, x=0x1000, w=0x2000, b=None, out=0x4000, lse=None, B=2, S=128, D=128, H=8,
          causal=1, key_len=None, dtype=1):
     return lib.mha_qkv_attention(x, w, b, out, lse, B, S, D, H, causal, key_len, dtype, None)

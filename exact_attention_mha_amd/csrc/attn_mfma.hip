@@ -943,15 +943,19 @@ static hipError_t launch_general(const AttnParams& p, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// 16-row query tiles, four waves sharing each K / V block (64 rows per
+// workgroup), row sums on the matrix cores: for problems with too few rows
+// to fill the chip with larger tiles, and (d_h <= 64) for causal problems,
+// whose triangle the small tiles balance better.
 template <typename T>
 static hipError_t launch_small(const AttnParams& p, hipStream_t s) {
   switch (p.D) {
     case 8: return launch_one<T, 8, 1, 1, 64, false>(p, s);
-    case 16: return launch_one<T, 16, 1, 1, 64, false>(p, s);
-    case 32: return launch_one<T, 32, 1, 1, 64, false>(p, s);
-    case 64: return launch_one<T, 64, 1, 1, 64, false>(p, s);
-    case 128: return launch_one<T, 128, 1, 1, 64, false>(p, s);
-    case 256: return launch_one<T, 256, 1, 1, 32, false>(p, s);
+    case 16: return launch_one<T, 16, 1, 4, 64, true>(p, s);
+    case 32: return launch_one<T, 32, 1, 4, 64, true>(p, s);
+    case 64: return launch_one<T, 64, 1, 4, 64, true>(p, s);
+    case 128: return launch_one<T, 128, 1, 4, 64, true>(p, s);
+    case 256: return launch_one<T, 256, 1, 4, 32, true>(p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -22,23 +22,35 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 
 bool supported_d(int64_t d) { return d == 8 || d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
 
+// Matrix-core tile choice (measured on MI355X over B, H, S, d_h, mask and
+// dtype): 16-row tiles in four-wave workgroups for
+//  * d_h 16 and 32 at every size measured,
+//  * d_h 64 below ~8 workgroups per CU of 128-row tiles, and for causal
+//    bf16 at any size (the general bf16 d_h 64 tile is the one without the
+//    pipelined loop),
+//  * any d_h with fewer than ~2 workgroups per CU of 128-row tiles;
+// the general tiled kernels otherwise.
+int choose_mfma(int64_t B, int64_t H, int64_t S, int64_t D, int causal, int dtype) {
+  const int64_t wg128 = B * H * ((S + 127) / 128);
+  if (D == 16 || D == 32) return MHA_VARIANT_MFMA_SMALL;
+  if (D == 64 && (wg128 < 2048 || (dtype == MHA_BF16 && causal))) return MHA_VARIANT_MFMA_SMALL;
+  if (wg128 < 512) return MHA_VARIANT_MFMA_SMALL;
+  return MHA_VARIANT_MFMA;
+}
+
 // Static kernel choice by regime (dtype, d_h, sequence length, head count):
 //  * fp32 inputs                         -> fp32 matrix-core kernel
 //  * S <= 128 and d_h <= 16              -> one pass per head, no LDS (any
 //                                           head count: few heads are split
 //                                           over four waves each)
 //  * S <= 128 and d_h <= 64, many heads  -> one pass per head, no rescaling
-//  * few heads (fewer than ~2 workgroups per CU with 128-row tiles)
-//                                        -> 16-row tiles, one wave each
-//  * otherwise                           -> general tiled kernel
-int choose(int64_t B, int64_t H, int64_t S, int64_t D, int dtype) {
+//  * otherwise                           -> matrix-core tiles (choose_mfma)
+int choose(int64_t B, int64_t H, int64_t S, int64_t D, int causal, int dtype) {
   if (dtype == MHA_F32) return MHA_VARIANT_F32;
   const int64_t heads = B * H;
   if (S <= 128 && D <= 16) return MHA_VARIANT_SHORT;
   if (S <= 128 && D <= 64 && heads >= 512) return MHA_VARIANT_SHORT;
-  const int64_t wg128 = heads * ((S + 127) / 128);
-  if (wg128 < 512) return MHA_VARIANT_MFMA_SMALL;
-  return MHA_VARIANT_MFMA;
+  return choose_mfma(B, H, S, D, causal, dtype);
 }
 
 int validate(const void* q, const void* k, const void* v, void* out, const float* lse,
@@ -79,7 +91,7 @@ int mha_forward_variant(const void* q, const void* k, const void* v, void* out, 
   if (st != MHA_OK) return st;
   if (variant < 0 || variant >= MHA_VARIANT_COUNT) return MHA_ERR_UNSUPPORTED;
   if (B == 0 || H == 0 || S == 0) return MHA_OK;
-  if (variant == MHA_VARIANT_AUTO) variant = choose(B, H, S, d_h, dtype);
+  if (variant == MHA_VARIANT_AUTO) variant = choose(B, H, S, d_h, causal, dtype);
   if (!variant_runs(variant, S, d_h, dtype)) return MHA_ERR_UNSUPPORTED;
 
   mha::AttnParams p;
@@ -127,9 +139,9 @@ int mha_forward_strided(const void* q, const void* k, const void* v, void* out, 
     if ((sb * esize) % 16 || (sh * esize) % 16 || (ss * esize) % 16) return MHA_ERR_MISALIGNED;
     if (((S - 1) * ss + d_h) * esize >= ((int64_t)1 << 31)) return MHA_ERR_SHAPE;
   }
-  int variant = choose(B, H, S, d_h, dtype);
+  int variant = choose(B, H, S, d_h, causal, dtype);
   if (variant == MHA_VARIANT_SHORT && d_h > 16)  // the d_h 32/64 short kernel is contiguous only
-    variant = B * H * ((S + 127) / 128) < 512 ? MHA_VARIANT_MFMA_SMALL : MHA_VARIANT_MFMA;
+    variant = choose_mfma(B, H, S, d_h, causal, dtype);
 
   mha::AttnParams p;
   p.q = q;
@@ -196,8 +208,8 @@ int mha_forward_train(const void* q, const void* k, const void* v, void* out, fl
   p.lay = mha::contiguous_layout((int)H, (int)S, (int)d_h);
   p.lay.k_b = p.lay.v_b = H_kv * S * d_h;  // k, v: contiguous [B, H_kv, S, d_h]
   p.lay.group = (int)(H / H_kv);
-  // the matrix-core kernels (the only ones that write out32), by head count
-  const bool small = B * H * ((S + 127) / 128) < 512;
+  // the matrix-core kernels (the only ones that write out32)
+  const bool small = choose_mfma(B, H, S, d_h, causal, dtype) == MHA_VARIANT_MFMA_SMALL;
   const hipError_t e = small ? mha::launch_mfma_small(p, (hipStream_t)stream)
                              : mha::launch_mfma(p, (hipStream_t)stream);
   if (e == hipErrorInvalidConfiguration) return MHA_ERR_SHAPE;
@@ -365,11 +377,10 @@ int mha_qkv_attention(const void* x, const void* w_qkv, const void* b_qkv, void*
 }
 
 int mha_select_variant(int64_t B, int64_t H, int64_t S, int64_t d_h, int causal, int dtype) {
-  (void)causal;
   if (B < 0 || H < 0 || S < 0 || d_h <= 0) return -MHA_ERR_SHAPE;
   if (dtype != MHA_F32 && dtype != MHA_F16 && dtype != MHA_BF16) return -MHA_ERR_UNSUPPORTED;
   if (!supported_d(d_h) || (d_h == 8 && dtype == MHA_F32)) return -MHA_ERR_UNSUPPORTED;
-  return choose(B, H, S, d_h, dtype);
+  return choose(B, H, S, d_h, causal ? 1 : 0, dtype);
 }
 
 const char* mha_variant_name(int variant) {

@@ -88,6 +88,14 @@ def test_variant_selection(mha):
     assert sel(10000, 8, 128, 16, True, torch.float16) == "short"
     assert sel(16, 4, 1024, 256, False, torch.float16) == "mfma"
     assert sel(32, 16, 100000, 64, True, torch.float16) == "mfma"
+    # 16-row four-wave tiles: d_h 16 / 32, mid-size d_h 64, causal bf16 d_h 64
+    assert sel(16, 16, 1024, 16, True, torch.float16) == "mfma_small"
+    assert sel(16, 16, 2048, 32, False, torch.bfloat16) == "mfma_small"
+    assert sel(4, 12, 1024, 64, True, torch.bfloat16) == "mfma_small"
+    assert sel(16, 12, 1024, 64, True, torch.float16) == "mfma_small"
+    assert sel(32, 16, 1024, 64, True, torch.bfloat16) == "mfma_small"
+    assert sel(16, 16, 2048, 64, False, torch.bfloat16) == "mfma"
+    assert sel(8, 16, 2048, 128, True, torch.float16) == "mfma"
     with pytest.raises(mha.MhaError):
         sel(1, 1, 16, 48, False, torch.float16)
 

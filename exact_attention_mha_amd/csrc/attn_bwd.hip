@@ -111,7 +111,7 @@ struct DqLds {
 
 template <typename T, int D, int NQT, int NW, int BK, int MODE>
 __device__ __forceinline__ void bwd_dq_body(
-    uint32_t blk, uint32_t nblk_grid, T* __restrict__ smem, const T* __restrict__ Qp,
+    uint32_t bh, int qb, T* __restrict__ smem, const T* __restrict__ Qp,
     const T* __restrict__ Kp, const T* __restrict__ Vp,
     const T* __restrict__ dOp, const float* __restrict__ LSEp, T* __restrict__ dQp,
     float* __restrict__ Dp, const int32_t* __restrict__ key_len, int H, int S, int causal,
@@ -134,10 +134,7 @@ __device__ __forceinline__ void bwd_dq_body(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
 
-  const uint32_t logical = xcd_logical_id(blk, nblk_grid);
-  const uint32_t bh = logical / (uint32_t)n_qblk;
-  int qb = (int)(logical - bh * (uint32_t)n_qblk);
-  if (causal) qb = n_qblk - 1 - qb;  // heaviest causal tiles first
+  // (batch, head) bh over B * H, query block qb
   const int b = (int)(bh / (uint32_t)H);
   const int L = clamp_len(key_len, b, S);
   const int64_t head = (int64_t)bh * S * D;
@@ -377,7 +374,7 @@ struct DkvLds {
 
 template <typename T, int D, int NKTW, int NW, int BQb>
 __device__ __forceinline__ void bwd_dkv_body(
-    uint32_t blk, uint32_t nblk_grid, T* __restrict__ smem, float* __restrict__ svec,
+    uint32_t bh, int kb, T* __restrict__ smem, float* __restrict__ svec,
     const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
     const T* __restrict__ dOp, const float* __restrict__ LSEp, const float* __restrict__ Dp,
     T* __restrict__ dKp, T* __restrict__ dVp, const int32_t* __restrict__ key_len, int H, int S,
@@ -403,10 +400,8 @@ __device__ __forceinline__ void bwd_dkv_body(
   // one workgroup per (batch, key / value head, key block); it walks the
   // query blocks of every query head of the group, so the key / value
   // gradients of grouped-query attention are complete without atomics
+  // (batch, key / value head) bh over B * Hk, key block kb
   const int Hk = H / group;
-  const uint32_t logical = xcd_logical_id(blk, nblk_grid);
-  const uint32_t bh = logical / (uint32_t)n_kblk;  // over B * Hk
-  const int kb = (int)(logical - bh * (uint32_t)n_kblk);
   const int b = (int)(bh / (uint32_t)Hk);
   const int L = clamp_len(key_len, b, S);
   const int64_t head = (int64_t)bh * S * D;        // K, V, dK, dV
@@ -630,39 +625,73 @@ attn_bwd_dq(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restr
             T* __restrict__ dQp, float* __restrict__ Dp, const int32_t* __restrict__ key_len,
             int H, int S, int causal, int n_qblk, float c_log2, float scale, int group) {
   __shared__ __attribute__((aligned(16))) char lds[DqLds<T, D, BK, NW>::BYTES];
-  bwd_dq_body<T, D, NQT, NW, BK, MODE>(blockIdx.x, gridDim.x, (T*)lds, Qp, Kp, Vp, dOp, LSEp,
+  const uint32_t logical = xcd_logical_id(blockIdx.x, gridDim.x);
+  const uint32_t bh = logical / (uint32_t)n_qblk;
+  int qb = (int)(logical - bh * (uint32_t)n_qblk);
+  if (causal) qb = n_qblk - 1 - qb;  // heaviest causal tiles first
+  bwd_dq_body<T, D, NQT, NW, BK, MODE>(bh, qb, (T*)lds, Qp, Kp, Vp, dOp, LSEp,
                                        dQp, Dp, key_len, H, S, causal, n_qblk, c_log2, scale, group);
 }
 
-// Both kinds in one launch, once the row term D is in the workspace: the
-// first n_kv_pad blocks are key-side blocks (n_kv of them live; the count is
-// padded to a multiple of 8 so that both kinds keep their XCD-aware order),
-// the rest query-side blocks reading D. The two kinds share the workgroup's
-// LDS; a causal problem's heaviest blocks of each kind start first, and
-// the lighter ones of both fill the machine behind them instead of each
-// kernel ending on its own partly empty tail.
+// Both kinds in one launch, once the row term D is in the workspace; the two
+// kinds share the workgroup's LDS. Two orders of the workgroups:
+//  * by level (causal problems of up to 4096 workgroups): level l holds key
+//    block l of every key / value head (n_hk of them) and query block
+//    n - 1 - l of every query head (n_hq), so the heaviest blocks of both
+//    kinds start first and the lighter levels fill in behind them (a key
+//    block's work falls with its index, a query block's grows with it);
+//    item r of a level (n_hk + n_hq padded to a multiple of 8) runs on XCD
+//    r % 8, so the blocks of one head share that XCD's L2 at every level.
+//    Ordered by kind instead, every key block of such a problem is resident
+//    before the first query block starts, and the heaviest query blocks
+//    finish last.
+//  * by kind (otherwise): the first n_kv_pad workgroups are key blocks (n_kv
+//    live, padded to a multiple of 8), then the query blocks, each kind in
+//    XCD-aware order (a head's blocks contiguous on one XCD), which larger
+//    problems need for L2 reuse.
 template <typename T, int D, int NQT, int NW, int BK, int NKTW, int BQb>
 __global__ void __launch_bounds__(NW * 64, 2)
 attn_bwd_both(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
               const T* __restrict__ dOp, const float* __restrict__ LSEp, const float* __restrict__ Dp,
               T* __restrict__ dQp, T* __restrict__ dKp, T* __restrict__ dVp,
-              const int32_t* __restrict__ key_len, int H, int S, int causal, int n_qblk,
-              int n_kblk, uint32_t n_kv, uint32_t n_kv_pad, uint32_t n_q, float c_log2,
+              const int32_t* __restrict__ key_len, int H, int S, int causal, int n_blk,
+              uint32_t n_hk, uint32_t n_hq, uint32_t per_xcd, int by_level, float c_log2,
               float scale, int group) {
   typedef DkvLds<T, D, BQb, NW> KvLds;
   constexpr int BYTES = KvLds::BYTES > DqLds<T, D, BK, NW>::BYTES ? KvLds::BYTES
                                                                   : DqLds<T, D, BK, NW>::BYTES;
   __shared__ __attribute__((aligned(16))) char lds[BYTES];
-  const uint32_t id = blockIdx.x;  // wave-uniform
-  if (id < n_kv_pad) {
-    if (id < n_kv)
-      bwd_dkv_body<T, D, NKTW, NW, BQb>(id, n_kv, (T*)lds, (float*)(lds + KvLds::TILE_BYTES), Qp,
-                                        Kp, Vp, dOp, LSEp, Dp, dKp, dVp, key_len, H, S, causal,
-                                        n_kblk, c_log2, scale, group);
+  // wave-uniform: this workgroup's kind, head and block
+  bool kv = false, live = true;
+  uint32_t bh = 0;
+  int blk = 0;
+  if (by_level) {
+    const uint32_t x = blockIdx.x & 7u, j = blockIdx.x >> 3;
+    const uint32_t level = j / per_xcd;
+    const uint32_t r = (j - level * per_xcd) * 8u + x;
+    kv = r < n_hk;
+    live = r < n_hk + n_hq;
+    bh = kv ? r : r - n_hk;
+    blk = kv ? (int)level : n_blk - 1 - (int)level;
   } else {
-    bwd_dq_body<T, D, NQT, NW, BK, kRowRead>(id - n_kv_pad, n_q, (T*)lds, Qp, Kp, Vp, dOp,
-                                             LSEp, dQp, const_cast<float*>(Dp), key_len, H, S,
-                                             causal, n_qblk, c_log2, scale, group);
+    const uint32_t n_kv = n_hk * (uint32_t)n_blk, n_kv_pad = (n_kv + 7u) & ~7u;
+    kv = blockIdx.x < n_kv_pad;
+    live = !kv || blockIdx.x < n_kv;
+    const uint32_t logical = kv ? xcd_logical_id(blockIdx.x, n_kv)
+                                : xcd_logical_id(blockIdx.x - n_kv_pad, n_hq * (uint32_t)n_blk);
+    bh = logical / (uint32_t)n_blk;
+    blk = (int)(logical - bh * (uint32_t)n_blk);
+    if (!kv && causal) blk = n_blk - 1 - blk;  // heaviest causal tiles first
+  }
+  if (!live) return;
+  if (kv) {
+    bwd_dkv_body<T, D, NKTW, NW, BQb>(bh, blk, (T*)lds, (float*)(lds + KvLds::TILE_BYTES), Qp, Kp,
+                                      Vp, dOp, LSEp, Dp, dKp, dVp, key_len, H, S, causal, n_blk,
+                                      c_log2, scale, group);
+  } else {
+    bwd_dq_body<T, D, NQT, NW, BK, kRowRead>(bh, blk, (T*)lds, Qp, Kp, Vp, dOp, LSEp, dQp,
+                                             const_cast<float*>(Dp), key_len, H, S, causal, n_blk,
+                                             c_log2, scale, group);
   }
 }
 
@@ -729,13 +758,18 @@ static hipError_t launch_bwd_one(const BwdParams& p, hipStream_t s) {
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
-  const int64_t wk_pad = (wk + 7) / 8 * 8;
-  if (wk_pad + wq > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_bwd_both<T, D, NQT, NW, BK, NKTW, BQb>), dim3((unsigned)(wk_pad + wq)),
+  // one level per block index (key and query blocks are the same size)
+  static_assert(BQ == BKW, "levels pair key block l with query block l");
+  const int64_t n_hk = (int64_t)p.B * (p.H / p.group), n_hq = (int64_t)p.B * p.H;
+  const int64_t per_xcd = (n_hk + n_hq + 7) / 8;
+  const int by_level = p.causal && per_xcd * 8 * n_qblk <= 4096;
+  const int64_t n_wg = by_level ? per_xcd * 8 * n_qblk : (wk + 7) / 8 * 8 + wq;
+  if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((attn_bwd_both<T, D, NQT, NW, BK, NKTW, BQb>), dim3((unsigned)n_wg),
                      dim3(NW * 64), 0, s, (const T*)p.q, (const T*)p.k, (const T*)p.v,
                      (const T*)p.dout, p.lse, p.delta, (T*)p.dq, (T*)p.dk, (T*)p.dv, p.key_len,
-                     p.H, p.S, p.causal, n_qblk, n_kblk, (uint32_t)wk, (uint32_t)wk_pad,
-                     (uint32_t)wq, p.c_log2, scale, p.group);
+                     p.H, p.S, p.causal, n_qblk, (uint32_t)n_hk, (uint32_t)n_hq,
+                     (uint32_t)per_xcd, by_level, p.c_log2, scale, p.group);
   return hipGetLastError();
 }
 

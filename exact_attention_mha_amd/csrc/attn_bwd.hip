@@ -635,7 +635,7 @@ attn_bwd_dq(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restr
 
 // Both kinds in one launch, once the row term D is in the workspace; the two
 // kinds share the workgroup's LDS. Two orders of the workgroups:
-//  * by level (causal problems of up to 4096 workgroups): level l holds key
+//  * by level (causal multi-head problems of up to 4096 workgroups): level l holds key
 //    block l of every key / value head (n_hk of them) and query block
 //    n - 1 - l of every query head (n_hq), so the heaviest blocks of both
 //    kinds start first and the lighter levels fill in behind them (a key
@@ -648,7 +648,9 @@ attn_bwd_dq(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restr
 //  * by kind (otherwise): the first n_kv_pad workgroups are key blocks (n_kv
 //    live, padded to a multiple of 8), then the query blocks, each kind in
 //    XCD-aware order (a head's blocks contiguous on one XCD), which larger
-//    problems need for L2 reuse.
+//    problems need for L2 reuse. With grouped heads a key block walks the
+//    query blocks of every head of its group, so the key blocks are the
+//    heavy kind and going first is already the better order.
 template <typename T, int D, int NQT, int NW, int BK, int NKTW, int BQb>
 __global__ void __launch_bounds__(NW * 64, 2)
 attn_bwd_both(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
@@ -762,7 +764,7 @@ static hipError_t launch_bwd_one(const BwdParams& p, hipStream_t s) {
   static_assert(BQ == BKW, "levels pair key block l with query block l");
   const int64_t n_hk = (int64_t)p.B * (p.H / p.group), n_hq = (int64_t)p.B * p.H;
   const int64_t per_xcd = (n_hk + n_hq + 7) / 8;
-  const int by_level = p.causal && per_xcd * 8 * n_qblk <= 4096;
+  const int by_level = p.causal && p.group == 1 && per_xcd * 8 * n_qblk <= 4096;
   const int64_t n_wg = by_level ? per_xcd * 8 * n_qblk : (wk + 7) / 8 * 8 + wq;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((attn_bwd_both<T, D, NQT, NW, BK, NKTW, BQb>), dim3((unsigned)n_wg),

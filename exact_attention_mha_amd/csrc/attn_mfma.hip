@@ -66,7 +66,10 @@ __device__ __forceinline__ int v_key_of_row(int rho) {
 
 // Four-wave workgroups ask for two of them per CU (two waves per SIMD), which
 // also keeps matrix-core results in ordinary VGPRs.
-template <typename T, int D, int NQT, int NW, int BK, bool SUM_MFMA, int NST, bool STALE = false>
+// SPLITP: fp16 probabilities enter the value product as a head and a
+// remainder too (bf16 always does), for an output exact to fp32 rounding.
+template <typename T, int D, int NQT, int NW, int BK, bool SUM_MFMA, int NST, bool STALE = false,
+          bool SPLITP = false>
 __global__ void __launch_bounds__(NW * 64, NW == 4 ? 2 : 1)
 attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
               T* __restrict__ Op, float* __restrict__ LSEp, float* __restrict__ O32p,
@@ -90,7 +93,7 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   constexpr int NKC = D >= 32 ? D / 32 : 1;
   constexpr int ES = (int)sizeof(T);
   constexpr int BQ = NW * NQT * 16;
-  constexpr bool kBf16 = __is_same(T, bf16_t);
+  constexpr bool kBf16 = __is_same(T, bf16_t) || SPLITP;  // probabilities as head + remainder
   static_assert(BK % 32 == 0 && (D % 16 == 0 || D == 8), "tile shape");
 
   __shared__ __attribute__((aligned(16))) T smem[NST * 2 * TILE];  // [stage][K, V]
@@ -355,7 +358,7 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             uint32_t hi, lo;
-            split2_bf16(a[2 * w], a[2 * w + 1], hi, lo);
+            split2<T>(a[2 * w], a[2 * w + 1], hi, lo);
             set_word(pf[t], w, hi);
             set_word(pl[t], w, lo);
           }
@@ -503,7 +506,7 @@ attn_fwd_mfma(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
 // resident with block kb, so the copies rotate over four LDS stages (block
 // kb+2 in flight). All LDS reads go through inline asm with explicit
 // lgkmcnt waits, counted over one stream of reads per step.
-template <typename T, int D, int NQT, int NW, int BK, int MINB>
+template <typename T, int D, int NQT, int NW, int BK, int MINB, bool SPLITP = false>
 __global__ void __launch_bounds__(NW * 64, MINB)
 attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
               T* __restrict__ Op, float* __restrict__ LSEp, float* __restrict__ O32p,
@@ -523,7 +526,7 @@ attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   constexpr int NKC = D / 32;
   constexpr int ES = (int)sizeof(T);
   constexpr int BQ = NW * NQT * 16;
-  constexpr bool kBf16 = __is_same(T, bf16_t);
+  constexpr bool kBf16 = __is_same(T, bf16_t) || SPLITP;  // probabilities as head + remainder
   constexpr uint32_t kStage = 2 * TILE * ES;  // bytes per LDS stage (K tile, V tile)
   static_assert(BK % 32 == 0 && D % 32 == 0, "tile shape");
   static_assert(TILE * ES < 65536, "ds_read offsets within a tile");
@@ -666,7 +669,7 @@ attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         uint32_t hi, lo;
-        split2_bf16(a[2 * j], a[2 * j + 1], hi, lo);
+        split2<T>(a[2 * j], a[2 * j + 1], hi, lo);
         set_word(pf[t], 2 * hh + j, hi);
         set_word(pl[t], 2 * hh + j, lo);
       }
@@ -892,25 +895,26 @@ attn_fwd_pipe(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __res
   }
 }
 
-template <typename T, int D, int NQT, int NW, int BK, bool SM, int NST = 2, bool STALE = false>
+template <typename T, int D, int NQT, int NW, int BK, bool SM, int NST = 2, bool STALE = false,
+          bool SPLITP = false>
 static hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   constexpr int BQ = NW * NQT * 16;
   const int n_qblk = (p.S + BQ - 1) / BQ;
   const int64_t n_wg = (int64_t)p.B * p.H * n_qblk;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_fwd_mfma<T, D, NQT, NW, BK, SM, NST, STALE>), dim3((unsigned)n_wg), dim3(NW * 64), 0, s,
+  hipLaunchKernelGGL((attn_fwd_mfma<T, D, NQT, NW, BK, SM, NST, STALE, SPLITP>), dim3((unsigned)n_wg), dim3(NW * 64), 0, s,
                      (const T*)p.q, (const T*)p.k, (const T*)p.v, (T*)p.out, p.lse, p.out32,
                      p.key_len, p.H, p.S, p.causal, n_qblk, p.c_log2, p.lay);
   return hipGetLastError();
 }
 
-template <typename T, int D, int NQT, int NW, int BK, int MINB>
+template <typename T, int D, int NQT, int NW, int BK, int MINB, bool SPLITP = false>
 static hipError_t launch_pipe(const AttnParams& p, hipStream_t s) {
   constexpr int BQ = NW * NQT * 16;
   const int n_qblk = (p.S + BQ - 1) / BQ;
   const int64_t n_wg = (int64_t)p.B * p.H * n_qblk;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_fwd_pipe<T, D, NQT, NW, BK, MINB>), dim3((unsigned)n_wg), dim3(NW * 64), 0, s,
+  hipLaunchKernelGGL((attn_fwd_pipe<T, D, NQT, NW, BK, MINB, SPLITP>), dim3((unsigned)n_wg), dim3(NW * 64), 0, s,
                      (const T*)p.q, (const T*)p.k, (const T*)p.v, (T*)p.out, p.lse, p.out32,
                      p.key_len, p.H, p.S, p.causal, n_qblk, p.c_log2, p.lay);
   return hipGetLastError();
@@ -957,6 +961,47 @@ static hipError_t launch_small(const AttnParams& p, hipStream_t s) {
     case 128: return launch_one<T, 128, 1, 4, 64, true>(p, s);
     case 256: return launch_one<T, 256, 1, 4, 32, true>(p, s);
   }
+  return hipErrorInvalidValue;
+}
+
+// The training forward's fp16 kernels: probabilities as head + remainder in
+// the value product (the tiles bf16 uses, which carry the same pairs), so
+// that the fp32 output the backward's row term comes from is exact to fp32
+// rounding for both dtypes. bf16 runs its ordinary kernels.
+static hipError_t launch_general_split(const AttnParams& p, hipStream_t s) {
+  typedef f16_t T;
+  switch (p.D) {
+    case 8: return launch_one<T, 8, 2, 4, 64, false, 2, false, true>(p, s);
+    case 16: return launch_one<T, 16, 2, 4, 64, false, 2, false, true>(p, s);
+    case 32: return launch_one<T, 32, 2, 4, 64, false, 2, false, true>(p, s);
+    case 64: return launch_one<T, 64, 4, 4, 64, true, 2, false, true>(p, s);
+    case 128: return launch_pipe<T, 128, 2, 8, 64, 1, true>(p, s);
+    case 256: return launch_one<T, 256, 2, 8, 32, true, 2, false, true>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+static hipError_t launch_small_split(const AttnParams& p, hipStream_t s) {
+  typedef f16_t T;
+  switch (p.D) {
+    case 8: return launch_one<T, 8, 1, 1, 64, false, 2, false, true>(p, s);
+    case 16: return launch_one<T, 16, 1, 4, 64, true, 2, false, true>(p, s);
+    case 32: return launch_one<T, 32, 1, 4, 64, true, 2, false, true>(p, s);
+    case 64: return launch_one<T, 64, 1, 4, 64, true, 2, false, true>(p, s);
+    case 128: return launch_one<T, 128, 1, 4, 64, true, 2, false, true>(p, s);
+    case 256: return launch_one<T, 256, 1, 4, 32, true, 2, false, true>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_mfma_train(const AttnParams& p, hipStream_t s) {
+  if (p.dtype == 1) return launch_general_split(p, s);
+  if (p.dtype == 2) return launch_general<bf16_t>(p, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_mfma_small_train(const AttnParams& p, hipStream_t s) {
+  if (p.dtype == 1) return launch_small_split(p, s);
+  if (p.dtype == 2) return launch_small<bf16_t>(p, s);
   return hipErrorInvalidValue;
 }
 

@@ -87,6 +87,9 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t s);          // dq then dk
 
 hipError_t launch_mfma(const AttnParams& p, hipStream_t s);        // general tiled, 16x16 products
 hipError_t launch_mfma_small(const AttnParams& p, hipStream_t s);  // few rows per WG
+// the same for the training forward (fp16 probabilities as head + remainder)
+hipError_t launch_mfma_train(const AttnParams& p, hipStream_t s);
+hipError_t launch_mfma_small_train(const AttnParams& p, hipStream_t s);
 hipError_t launch_f32(const AttnParams& p, hipStream_t s);         // fp32 inputs
 hipError_t launch_valu_d16(const AttnParams& p, hipStream_t s);    // d_h = 16 VALU
 hipError_t launch_short(const AttnParams& p, hipStream_t s);       // S <= 128 one pass, d_h 32/64

@@ -208,10 +208,11 @@ int mha_forward_train(const void* q, const void* k, const void* v, void* out, fl
   p.lay = mha::contiguous_layout((int)H, (int)S, (int)d_h);
   p.lay.k_b = p.lay.v_b = H_kv * S * d_h;  // k, v: contiguous [B, H_kv, S, d_h]
   p.lay.group = (int)(H / H_kv);
-  // the matrix-core kernels (the only ones that write out32)
+  // the matrix-core kernels (the only ones that write out32), with fp16
+  // probabilities as head + remainder in the value product
   const bool small = choose_mfma(B, H, S, d_h, causal, dtype) == MHA_VARIANT_MFMA_SMALL;
-  const hipError_t e = small ? mha::launch_mfma_small(p, (hipStream_t)stream)
-                             : mha::launch_mfma(p, (hipStream_t)stream);
+  const hipError_t e = small ? mha::launch_mfma_small_train(p, (hipStream_t)stream)
+                             : mha::launch_mfma_train(p, (hipStream_t)stream);
   if (e == hipErrorInvalidConfiguration) return MHA_ERR_SHAPE;
   return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
 }

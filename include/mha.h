@@ -121,10 +121,11 @@ int mha_forward_variant(const void* q, const void* k, const void* v, void* out, 
  * attention") takes its softmax row term from dout and the forward output,
  * D = rowsum(dout * O). With O rounded to fp16 or bf16 that term is off by a
  * rounding of O, which dq and dk amplify where the softmax is peaked; the
- * output before that rounding (O / l in fp32) keeps it within the accuracy
- * rule over the range of scores stated for mha_backward, and lets the
- * backward form D with one pass over dout and out32 instead of a pass over
- * the keys.
+ * output before that rounding (O / l in fp32, with the probabilities
+ * entering the value product as a head and a remainder for both dtypes)
+ * keeps it within the accuracy rule over the range of scores stated for
+ * mha_backward, and lets the backward form D with one pass over dout and
+ * out32 instead of a pass over the keys.
  *
  *   out32    device pointer, contiguous fp32 [B, H, S, d_h], 16-byte aligned;
  *            written in full (rows with no visible key get 0). Required.
@@ -134,9 +135,11 @@ int mha_forward_variant(const void* q, const void* k, const void* v, void* out, 
  *            in mha_forward_strided (H_kv = H: ordinary multi-head).
  *   other arguments as for mha_forward; dtype must be MHA_F16 or MHA_BF16.
  *
- * Runs the matrix-core kernels (out is identical to what mha_forward_variant
- * writes with MHA_VARIANT_MFMA or MHA_VARIANT_MFMA_SMALL, chosen by head
- * count as mha_forward does for long sequences). Returns MHA_ERR_UNSUPPORTED
+ * Runs the matrix-core kernels, chosen by size as mha_forward does for long
+ * sequences. For bf16, out is identical to what mha_forward_variant writes
+ * with MHA_VARIANT_MFMA or MHA_VARIANT_MFMA_SMALL; for fp16 the head and
+ * remainder probabilities can move out by a rounding against mha_forward's
+ * (out is always out32 rounded once). Returns MHA_ERR_UNSUPPORTED
  * for fp32 inputs, MHA_ERR_NULL without lse or out32, MHA_ERR_SHAPE when one
  * head of out32 spans 2^31 bytes or more or H_kv does not divide H. Ownership, asynchrony and error
  * behaviour as for mha_forward.
@@ -272,11 +275,9 @@ int mha_backward_grouped(const void* q, const void* k, const void* v, const void
  *   other arguments as mha_backward_grouped (H_kv = H for ordinary
  *   multi-head attention).
  *
- * Precision as mha_backward for bf16 (the forward's probabilities enter its
- * value product as a head and a remainder, so out32 is the exact output to
- * fp32 rounding); for fp16 out32 carries the single rounding of the
- * probabilities in that product, which stays within the accuracy rule over
- * the range of scores stated for mha_backward. MHA_ERR_NULL without out32.
+ * Precision as mha_backward: out32 is the exact output to fp32 rounding (the
+ * training forward's probabilities enter its value product as a head and a
+ * remainder for both dtypes). MHA_ERR_NULL without out32.
  */
 int mha_backward_train(const void* q, const void* k, const void* v, const float* out32,
                        const void* dout, const float* lse, void* dq, void* dk, void* dv,

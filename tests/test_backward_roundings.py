@@ -78,12 +78,14 @@ def test_row_term_from_rounded_output_breaks_the_rule(dt):
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 def test_row_term_from_the_fp32_output_meets_the_rule(dt):
     """The training pair's reading: D = dO . O32 with O32 the forward's output
-    before its final rounding, built as the kernels build it (unnormalised
-    probabilities rounded to fp16, or to a bf16 head and remainder, in the
-    value product; fp32 accumulation; divided by the row sum of the rounded
-    probabilities) and the backward's P rebuilt from lse = m + ln(that sum).
-    On the peaked inputs where D from the rounded output misses the rule,
-    dq and dk built on it stay inside with margin."""
+    before its final rounding, built as the training forward builds it
+    (unnormalised probabilities as a head and a remainder in the input dtype
+    in the value product; fp32 accumulation; divided by the row sum of those
+    pairs) and the backward's P rebuilt from lse = m + ln(that sum). On the
+    peaked inputs where D from the rounded output misses the rule, dq and dk
+    built on it stay inside with margin; with the probabilities rounded
+    once (fp16), as the plain forward takes them, the margin shrinks to
+    about half the budget here and random cases at this scale crossed it."""
     q, k, v, do = _peaked(dt)
     rq, rk, _ = oracle.attention_backward(q, k, v, do, causal=True)
     S, D = q.shape[-2:]
@@ -94,17 +96,21 @@ def test_row_term_from_the_fp32_output_meets_the_rule(dt):
     def as_dt(x):
         return torch.from_numpy(x).to(torch.float32).to(DT[dt]).double().numpy()
 
-    pr = as_dt(e)
-    if dt == "bf16":
-        pr = pr + as_dt(e - pr)
-    l = pr.sum(axis=-1, keepdims=True)
-    o32 = torch.from_numpy((pr @ v) / l).float().double().numpy()
-    p = e / l
-    dp = do @ np.swapaxes(v, -1, -2)
-    ds = p * (dp - (do * o32).sum(axis=-1, keepdims=True))
-    gq, gk = as_dt(ds @ k * sc), as_dt(np.swapaxes(ds, -1, -2) @ q * sc)
-    assert oracle.budget_fraction(gq, rq) < 0.75
-    assert oracle.budget_fraction(gk, rk) < 0.75
+    def grads(pr):
+        l = pr.sum(axis=-1, keepdims=True)
+        o32 = torch.from_numpy((pr @ v) / l).float().double().numpy()
+        p = e / l
+        dp = do @ np.swapaxes(v, -1, -2)
+        ds = p * (dp - (do * o32).sum(axis=-1, keepdims=True))
+        return as_dt(ds @ k * sc), as_dt(np.swapaxes(ds, -1, -2) @ q * sc)
+
+    head = as_dt(e)
+    gq, gk = grads(head + as_dt(e - head))
+    assert oracle.budget_fraction(gq, rq) < 0.25
+    assert oracle.budget_fraction(gk, rk) < 0.25
+    if dt == "f16":
+        gq, gk = grads(head)
+        assert 0.25 < oracle.budget_fraction(gq, rq) < 1.0
 
 
 def _wide(seed=538493):

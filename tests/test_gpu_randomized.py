@@ -219,3 +219,44 @@ def test_randomized_variants_layouts_long_backward(mha, seed):
         causal = rng.random() < 0.5
         scale = rng.choice([1.0, 1.0, 3.0, 8.0])
         run[kind](mha, rng, g, causal, scale, case)
+
+
+def _training_case(mha, rng, g, causal, scale, case):
+    """The training pair: mha_forward_train's fp32 output against the
+    oracle's output, and mha_backward_train's gradients (row term from that
+    output) against the oracle's, for plain and grouped-query heads."""
+    D = rng.choice([16, 32, 64, 64, 128, 256])
+    dt = rng.choice(["f16", "bf16"])
+    S, B, Hk = rng.randint(1, 400), rng.randint(1, 3), rng.randint(1, 3)
+    H = Hk * rng.choice([1, 1, 2, 3])
+    q = torch.randn(B, H, S, D, generator=g).mul(min(scale, 3.0)).to(DT[dt])
+    k = torch.randn(B, Hk, S, D, generator=g).mul(min(scale, 3.0)).to(DT[dt])
+    v = torch.randn(B, Hk, S, D, generator=g).to(DT[dt])
+    do = torch.randn(B, H, S, D, generator=g).to(DT[dt])
+    kl = _key_len(rng, B, S)
+    label = f"case {case} train B{B} H{H}/{Hk} S{S} D{D} {dt} causal={causal} kl={kl}"
+    print(label, flush=True)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    kld = None if kl is None else kl.cuda()
+    out, lse, out32 = mha.forward_train(qd, kd, vd, causal=causal, key_len=kld)
+    dq, dk, dv = mha.backward_train(qd, kd, vd, out32, lse, dod, causal=causal, key_len=kld)
+    torch.cuda.synchronize()
+    grp = H // Hk
+    ke, ve = (t.repeat_interleave(grp, dim=1) for t in (k, v))
+    ro, rl = oracle.attention(q, ke, ve, causal=causal, key_len=kl, threads=THREADS)
+    rq, rk, rv = oracle.attention_backward(q, ke, ve, do, causal=causal, key_len=kl,
+                                           threads=THREADS)
+    rk = rk.reshape(B, Hk, grp, S, D).sum(axis=2)
+    rv = rv.reshape(B, Hk, grp, S, D).sum(axis=2)
+    _check(label, [("out", out.cpu(), ro), ("out32", out32.cpu(), ro), ("lse", lse.cpu(), rl),
+                   ("dq", dq.cpu(), rq), ("dk", dk.cpu(), rk), ("dv", dv.cpu(), rv)])
+
+
+@pytest.mark.parametrize("seed", [11, 12])
+def test_randomized_training_pair(mha, seed):
+    rng = random.Random(seed)
+    for case in range(100):
+        g = torch.Generator().manual_seed(case * 7919 + seed)
+        causal = rng.random() < 0.5
+        scale = rng.choice([1.0, 1.0, 2.0, 3.0])
+        _training_case(mha, rng, g, causal, scale, case)

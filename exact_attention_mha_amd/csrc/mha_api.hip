@@ -209,8 +209,9 @@ int mha_forward_train(const void* q, const void* k, const void* v, void* out, fl
   p.lay.k_b = p.lay.v_b = H_kv * S * d_h;  // k, v: contiguous [B, H_kv, S, d_h]
   p.lay.group = (int)(H / H_kv);
   // the matrix-core kernels (the only ones that write out32), with fp16
-  // probabilities as head + remainder in the value product
-  const bool small = choose_mfma(B, H, S, d_h, causal, dtype) == MHA_VARIANT_MFMA_SMALL;
+  // probabilities as head + remainder in the value product; the tiles are
+  // bf16's, and so is the choice between them
+  const bool small = choose_mfma(B, H, S, d_h, causal, MHA_BF16) == MHA_VARIANT_MFMA_SMALL;
   const hipError_t e = small ? mha::launch_mfma_small_train(p, (hipStream_t)stream)
                              : mha::launch_mfma_train(p, (hipStream_t)stream);
   if (e == hipErrorInvalidConfiguration) return MHA_ERR_SHAPE;

@@ -300,17 +300,36 @@ __device__ __forceinline__ void split2_bf16(float a, float b, uint32_t& hi, uint
   const float hb = __builtin_bit_cast(float, hi & 0xffff0000u);
   lo = pack2<bf16_t>(a - ha, b - hb);
 }
-// fp16 head + remainder of a pair, as above (the heads widened back to fp32;
-// a - head is exact in fp32 for |a| below the fp16 range)
+// a - (the fp16 number in the low / high half of h), in fp32: one
+// mixed-precision FMA, (-1) * h + a, that widens h itself (the same value as
+// widening h and subtracting)
+__device__ __forceinline__ float sub_f16_lo(uint32_t h, float a) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(a));
+  return r;
+}
+__device__ __forceinline__ float sub_f16_hi(uint32_t h, float a) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(a));
+  return r;
+}
+// fp16 head + remainder of a pair, as above (a - head is exact in fp32 for
+// |a| below the fp16 range)
 __device__ __forceinline__ void split2_f16(float a, float b, uint32_t& hi, uint32_t& lo) {
   hi = pack2<f16_t>(a, b);
-  const f32x2 h = __builtin_convertvector(__builtin_bit_cast(f16x2, hi), f32x2);
-  lo = pack2<f16_t>(a - h[0], b - h[1]);
+  lo = pack2<f16_t>(sub_f16_lo(hi, a), sub_f16_hi(hi, b));
 }
 template <typename T> __device__ __forceinline__ void split2(float a, float b, uint32_t& hi,
                                                               uint32_t& lo) {
   if constexpr (__is_same(T, bf16_t)) split2_bf16(a, b, hi, lo);
   else split2_f16(a, b, hi, lo);
+}
+// head + remainder of four values: elements 0-3 the heads, 4-7 the remainders
+template <typename T> __device__ __forceinline__ typename Vec<T>::x8 split4(const AccK32& a) {
+  uint32_t h0, l0, h1, l1;
+  split2<T>(a[0], a[1], h0, l0);
+  split2<T>(a[2], a[3], h1, l1);
+  return __builtin_bit_cast(typename Vec<T>::x8, u32x4{h0, h1, l0, l1});
 }
 // word j of an 8 x 16-bit operand
 template <typename V> __device__ __forceinline__ void set_word(V& v, int j, uint32_t w) {

@@ -226,19 +226,11 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
             av[i] = 16 * j + i >= vlim ? 0.f : av[i];  // V row 16j + 4g + i
           }
         }
-        T4 kh, kl, vh, vl;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          kh[i] = to_t<T>(ak[i]);
-          vh[i] = to_t<T>(av[i]);
-          kl[i] = to_t<T>(ak[i] - to_f(kh[i]));
-          if constexpr (kSplit) vl[i] = to_t<T>(av[i] - to_f(vh[i]));
-        }
-        kf[j] = __builtin_shufflevector(kh, kl, 0, 1, 2, 3, 4, 5, 6, 7);
+        kf[j] = split4<T>(ak);
         if constexpr (kSplit) {
-          vt[j] = __builtin_shufflevector(vh, vl, 0, 1, 2, 3, 4, 5, 6, 7);
+          vt[j] = split4<T>(av);
         } else {
-          vt[j] = vh;
+          vt[j] = __builtin_bit_cast(T4, u32x2{pack2<T>(av[0], av[1]), pack2<T>(av[2], av[3])});
         }
         __builtin_amdgcn_sched_barrier(0);  // one tile at a time (register pressure)
       });
@@ -274,11 +266,9 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
         read_tile(J, st_off, xf);
         AccK32 aq = bq, ak, av;
         project(std::integral_constant<int, 0>{}, xf, true, false, aq, ak, av);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          q4[i] = to_t<T>(aq[i]);
-          l4[i] = to_t<T>(aq[i] - to_f(q4[i]));
-        }
+        const T8 ql = split4<T>(aq);
+        q4 = __builtin_shufflevector(ql, ql, 0, 1, 2, 3);
+        l4 = __builtin_shufflevector(ql, ql, 4, 5, 6, 7);
       }
       constexpr int NKT = CAUSAL ? t + 1 : NT;  // key tiles computed at most
       const int klast = min(CAUSAL ? t : NT - 1, (L - 1) >> 4);
@@ -316,11 +306,15 @@ attn_qkv16(const T* __restrict__ Xp, const T* __restrict__ Wp, const T* __restri
         }
         m[j] = group_max(mx) * c_log2;  // finite: key 0 is visible
         auto probs = [&](const AccK32& sv, T4& hi, T4& lo) {
+          AccK32 pv;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float pv = fast_exp2(fmaf(sv[i], c_log2, -m[j]));
-            hi[i] = to_t<T>(pv);
-            if constexpr (kSplit) lo[i] = to_t<T>(pv - to_f(hi[i]));
+          for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(fmaf(sv[i], c_log2, -m[j]));
+          if constexpr (kSplit) {
+            const T8 pl = split4<T>(pv);
+            hi = __builtin_shufflevector(pl, pl, 0, 1, 2, 3);
+            lo = __builtin_shufflevector(pl, pl, 4, 5, 6, 7);
+          } else {
+            hi = __builtin_bit_cast(T4, u32x2{pack2<T>(pv[0], pv[1]), pack2<T>(pv[2], pv[3])});
           }
         };
         // all 16 value columns are multiplied; only head j's columns of

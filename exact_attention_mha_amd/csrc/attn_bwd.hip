@@ -289,11 +289,10 @@ __device__ __forceinline__ void bwd_dq_body(
           // 2 (kt % 2), 2 (kt % 2) + 1 of the pair's operand
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            const float d0 = s[t][kt][2 * j] * (dp[t][kt][2 * j] - drow[t]);
-            const float d1 = s[t][kt][2 * j + 1] * (dp[t][kt][2 * j + 1] - drow[t]);
             const int w = 2 * (kt & 1) + j;
             uint32_t dh, dlo;
-            split2<T>(d0, d1, dh, dlo);
+            split2_prod<T>(s[t][kt][2 * j], dp[t][kt][2 * j] - drow[t], s[t][kt][2 * j + 1],
+                           dp[t][kt][2 * j + 1] - drow[t], dh, dlo);
             set_word(dsf[t][kt >> 1], w, dh);
             set_word(dsl[t][kt >> 1], w, dlo);
           }
@@ -553,11 +552,9 @@ __device__ __forceinline__ void bwd_dkv_body(
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
               const float p0 = s[h][t][2 * j], p1 = s[h][t][2 * j + 1];
-              const float d0 = p0 * (dp[h][t][2 * j] - dv[2 * j]);
-              const float d1 = p1 * (dp[h][t][2 * j + 1] - dv[2 * j + 1]);
               uint32_t ph, plo, dh, dlo;
               split2<T>(p0, p1, ph, plo);
-              split2<T>(d0, d1, dh, dlo);
+              split2_prod<T>(p0, dp[h][t][2 * j] - dv[2 * j], p1, dp[h][t][2 * j + 1] - dv[2 * j + 1], dh, dlo);
               set_word(pf[t], 2 * h + j, ph);
               set_word(pl[t], 2 * h + j, plo);
               set_word(dsf[t], 2 * h + j, dh);

@@ -324,6 +324,24 @@ template <typename T> __device__ __forceinline__ void split2(float a, float b, u
   if constexpr (__is_same(T, bf16_t)) split2_bf16(a, b, hi, lo);
   else split2_f16(a, b, hi, lo);
 }
+// head + remainder of two products pa * xa, pb * xb: the heads are the
+// rounded products, the remainders come from one fused multiply-add each
+// (pa * xa - head, compiled to a mixed-precision FMA for fp16), so they also
+// carry the products' own fp32 rounding errors
+template <typename T> __device__ __forceinline__ void split2_prod(float pa, float xa, float pb, float xb,
+                                                                   uint32_t& hi, uint32_t& lo) {
+  hi = pack2<T>(pa * xa, pb * xb);
+  float ha, hb;
+  if constexpr (__is_same(T, bf16_t)) {
+    ha = __builtin_bit_cast(float, hi << 16);
+    hb = __builtin_bit_cast(float, hi & 0xffff0000u);
+  } else {
+    const f32x2 h = __builtin_convertvector(__builtin_bit_cast(f16x2, hi), f32x2);
+    ha = h[0];
+    hb = h[1];
+  }
+  lo = pack2<T>(fmaf(pa, xa, -ha), fmaf(pb, xb, -hb));
+}
 // head + remainder of four values: elements 0-3 the heads, 4-7 the remainders
 template <typename T> __device__ __forceinline__ typename Vec<T>::x8 split4(const AccK32& a) {
   uint32_t h0, l0, h1, l1;

@@ -189,6 +189,12 @@ __device__ __forceinline__ void bwd_dq_body(
   for (int t = 0; t < NQT; ++t)
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc_dq[t][dt] = AccK32::zero();
+  // dP^T accumulators start from -D of the lane's row (its query column),
+  // so the products leave dP - D; the row pass accumulates from zero
+  typedef std::conditional_t<D == 16, AccK16T<T>, AccK32> SAcc;  // K = 16 products at d_h = 16
+  SAcc dp0[NQT];
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) dp0[t] = SAcc::fill(MODE == kRowRead ? -drow[t] : 0.f);
 
   if (nblk > 0) {
     const rsrc_t rk = make_rsrc(Kp + head_kv, (uint32_t)kend * RB);
@@ -217,16 +223,17 @@ __device__ __forceinline__ void bwd_dq_body(
       const T* Ks = smem + (kb & 1) * 2 * Tile::ELEMS;
       const T* Vs = Ks + Tile::ELEMS;
 
-      // S^T = K Q^T and dP^T = V dO^T; key 16kt + 4g + i of the block in
-      // register i of lane (g, c)
-      // K = 16 products at d_h = 16, K = 32 ones otherwise
-      typedef std::conditional_t<D == 16, AccK16T<T>, AccK32> SAcc;
+      // S^T = K Q^T and dP^T - D = V dO^T - D; key 16kt + 4g + i of the
+      // block in register i of lane (g, c)
       SAcc s[NQT][NKT], dp[NQT][NKT];
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt) {
         const int rb = 16 * kt * STR + rrow;
 #pragma unroll
-        for (int t = 0; t < NQT; ++t) s[t][kt] = dp[t][kt] = SAcc::zero();
+        for (int t = 0; t < NQT; ++t) {
+          s[t][kt] = SAcc::zero();
+          dp[t][kt] = dp0[t];
+        }
         if constexpr (D == 16) {
           const T4 kf = *(const T4*)(Ks + rb + 4 * g);
           const T4 vf = *(const T4*)(Vs + rb + 4 * g);
@@ -250,6 +257,7 @@ __device__ __forceinline__ void bwd_dq_body(
       }
 
       // P = exp(S / sqrt(d) - lse) (0 for hidden pairs), dS = P (dP - D)
+      // (dp already holds dP - D in the row read mode)
       const bool edge = (k0 + BK > L) || (causal && (k0 + BK - 1 > wq0));
       T8 dsf[NQT][NKP], dsl[NQT][NKP];
 #pragma unroll
@@ -291,8 +299,8 @@ __device__ __forceinline__ void bwd_dq_body(
           for (int j = 0; j < 2; ++j) {
             const int w = 2 * (kt & 1) + j;
             uint32_t dh, dlo;
-            split2_prod<T>(s[t][kt][2 * j], dp[t][kt][2 * j] - drow[t], s[t][kt][2 * j + 1],
-                           dp[t][kt][2 * j + 1] - drow[t], dh, dlo);
+            split2_prod<T>(s[t][kt][2 * j], dp[t][kt][2 * j], s[t][kt][2 * j + 1], dp[t][kt][2 * j + 1],
+                           dh, dlo);
             set_word(dsf[t][kt >> 1], w, dh);
             set_word(dsl[t][kt >> 1], w, dlo);
           }
@@ -450,14 +458,21 @@ __device__ __forceinline__ void bwd_dkv_body(
     const int voff = lane < BQb ? 4 * lane : kOutOfRange;
     // iteration it covers query head j = it / nblk of the group, query
     // block it % nblk
-    auto dma_block = [&](int st, int it) {
-      const int j = it / nblk;
-      const int q0 = q_lo + (it - j * nblk) * BQb;
+    // the copies walk the iterations in order: (query head cj, block cqb)
+    // of the next copy advance by one each time (no division per block),
+    // and the buffer descriptors change only with the query head
+    int cj = 0, cqb = 0;
+    rsrc_t rq, rdo, rl, rd;
+    auto set_head = [&](int j) {
       const int64_t hq = (bhq0 + j) * S * D, hr = (bhq0 + j) * S;
-      const rsrc_t rq = make_rsrc(Qp + hq, (uint32_t)S * RB);
-      const rsrc_t rdo = make_rsrc(dOp + hq, (uint32_t)S * RB);
-      const rsrc_t rl = make_rsrc(LSEp + hr, (uint32_t)S * 4);
-      const rsrc_t rd = make_rsrc(Dp + hr, (uint32_t)S * 4);
+      rq = make_rsrc(Qp + hq, (uint32_t)S * RB);
+      rdo = make_rsrc(dOp + hq, (uint32_t)S * RB);
+      rl = make_rsrc(LSEp + hr, (uint32_t)S * 4);
+      rd = make_rsrc(Dp + hr, (uint32_t)S * 4);
+    };
+    set_head(0);
+    auto dma_next = [&](int st) {
+      const int q0 = q_lo + cqb * BQb;
       T* Qst = smem + st * 2 * Tile::ELEMS;
       Tile::copy(rq, Qst, off, wave, q0 * RB);
       Tile::copy(rdo, Qst + Tile::ELEMS, off, wave, q0 * RB);
@@ -465,19 +480,22 @@ __device__ __forceinline__ void bwd_dkv_body(
         dma4(rl, svec + st * 2 * ROWF, voff, q0 * 4);
         dma4(rd, svec + st * 2 * ROWF + ROWF, voff, q0 * 4);
       }
+      if (++cqb == nblk) {
+        cqb = 0;
+        if (++cj < group) set_head(cj);
+      }
     };
-    dma_block(0, 0);
+    dma_next(0);
 
     const int rrow = (D >= 32 ? c : bwd_lds_row(c)) * STR;
     const int trow = (D >= 32 ? 4 * g + (c >> 2) : bwd_lds_row(4 * g + (c >> 2))) * STR + 4 * (c & 3);
 
     const int n_it = group * nblk;
-    for (int it = 0; it < n_it; ++it) {
-      const int qb = it - (it / nblk) * nblk;
+    for (int it = 0, qb = 0; it < n_it; ++it, qb = qb + 1 == nblk ? 0 : qb + 1) {
       const int q0 = q_lo + qb * BQb;
       wait_vmem();
       block_barrier();
-      if (it + 1 < n_it) dma_block((it + 1) & 1, it + 1);
+      if (it + 1 < n_it) dma_next((it + 1) & 1);
 
       const T* Qs = smem + (it & 1) * 2 * Tile::ELEMS;
       const T* dOs = Qs + Tile::ELEMS;
